@@ -1,0 +1,193 @@
+/*
+ * paged_gqa.h -- C ABI of a gfx950 (MI355X) library for paged grouped-query
+ * attention with head_dim 256 over a block-table-indexed KV cache.
+ *
+ * Three calls, one per problem on the source pages:
+ *   paged_attn_verify          short multi-token speculative-verify queries
+ *                              (SGLang PR #36330, "... MTP unified attention on
+ *                              gfx950": Motivation, Modifications)
+ *   paged_attn_prefill_prefix  new tokens against a cached prefix with
+ *                              bottom-right causal masking (ROCm/ATOM PR #2534,
+ *                              "asm FP8 FMHA for prefix-hit prefill ...": the
+ *                              FMHA commit message and Summary)
+ *   sparse_paged_attn          each query row attends only its own list of
+ *                              selected tokens (vLLM PR #62590, "Tune sparse GQA
+ *                              prefill profile on gfx942 and gfx950": Overview,
+ *                              Earlier results)
+ *
+ * What every call computes, for sequence b, query token t (0 <= t < Lq_b) and
+ * query head h, with r = num_q_heads / num_kv_heads and g = h / r:
+ *   s_j  = softmax_scale * q_descale * k_descale * <q[t,h,:], K_j[g,:]>
+ *   out  = v_descale * sum_j softmax(s)_j * V_j[g,:]       (bf16, RNE)
+ *   lse  = ln sum_j exp(s_j)                                (fp32, optional)
+ * over the visible keys j: 0 <= j <= Lk_b - Lq_b + t (verify, prefill), or the
+ * entries of the row's index list that lie in [0, Lk_b) (sparse).  Lk_b counts
+ * the sequence's new tokens, so its last query token sees all Lk_b keys.  A row
+ * with no visible key gets out = 0 and lse = -inf.
+ *
+ * Memory.  Every pointer except `kv` (a host struct) is device memory owned by
+ * the caller; nothing is allocated, freed or retained by the library.  Q and
+ * out are row-major [T, num_q_heads, 256] with T = cu_seqlens_q[num_seqs]; lse
+ * is [T, num_q_heads].  Logical key j of sequence b lives in pool page
+ * block_table[b * block_table_stride + j / page_size], slot j % page_size; the
+ * element offset of (page, slot, kv head, d) is
+ *   page * stride_page + slot * stride_token + head * stride_head + d
+ * (strides in elements, d unit-stride), which covers [pages, slots, heads, d]
+ * and [pages, heads, slots, d] pools alike (ROCm/ATOM PR #2830, summary
+ * paragraph: the block-table stride is a runtime argument).
+ *
+ * Numbers.  BF16 or OCP FP8 E4M3FN codes; real value = code * descale.  The
+ * descales are per-tensor fp32 scalars in device memory (NULL means 1.0).
+ *
+ * Errors.  Every host-checkable condition is checked before anything is
+ * launched; on error the call returns a nonzero PGA_ERR_* code, launches
+ * nothing and leaves `out`, `lse` and the workspace untouched.  Device data is
+ * not validated (that would need a synchronisation): block-table entries
+ * outside [0, num_pages) are never dereferenced, but the result for a sequence
+ * that has one is undefined.  There is no silent fallback path.
+ *
+ * Threading.  Calls are asynchronous on `stream` (a hipStream_t; NULL is the
+ * default stream), hold no global mutable state and may run concurrently on
+ * different streams, provided their workspaces do not overlap.
+ */
+#ifndef PAGED_GQA_H_
+#define PAGED_GQA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PGA_ABI_VERSION 1
+#define PGA_HEAD_DIM 256
+
+/* Element encodings. */
+enum pga_dtype {
+  PGA_DTYPE_BF16 = 1,     /* bfloat16 */
+  PGA_DTYPE_FP8_E4M3 = 2  /* OCP FP8 E4M3FN (no infinities, max 448) */
+};
+
+/* Status codes. */
+enum pga_status {
+  PGA_OK = 0,
+  PGA_ERR_NULL = 1,        /* a required pointer is NULL */
+  PGA_ERR_SHAPE = 2,       /* head_dim != 256, Hq % Hkv != 0, negative sizes, q-length envelope */
+  PGA_ERR_DTYPE = 3,       /* unsupported dtype or q/kv dtype pair */
+  PGA_ERR_UNSUPPORTED = 4, /* outside the kernel envelope: page size, alignment, rows per group */
+  PGA_ERR_WORKSPACE = 5,   /* workspace smaller than the matching *_workspace_bytes() */
+  PGA_ERR_LAUNCH = 6       /* the HIP runtime refused a launch */
+};
+
+/* The paged KV cache.  K and V share dtype, head count and page size; their
+ * strides may differ.  All strides are in elements and must be multiples of
+ * 16 bytes' worth of elements; k_cache and v_cache must be 16-byte aligned. */
+typedef struct pga_paged_kv {
+  const void* k_cache;
+  const void* v_cache;
+  int32_t dtype;              /* enum pga_dtype */
+  int32_t num_kv_heads;       /* >= 1 */
+  int32_t head_dim;           /* must be 256 */
+  int32_t page_size;          /* tokens per page: a power of two, 16..1024 */
+  int32_t num_pages;          /* pages in the pool; entries outside [0, num_pages) are never read */
+  int32_t reserved;           /* set to 0 */
+  int64_t k_stride_page, k_stride_token, k_stride_head;
+  int64_t v_stride_page, v_stride_token, v_stride_head;
+  const int32_t* block_table; /* [num_seqs, block_table_stride] physical page ids */
+  int64_t block_table_stride; /* >= ceil(max KV length / page_size) */
+  const float* k_descale;     /* device scalar or NULL (1.0) */
+  const float* v_descale;     /* device scalar or NULL (1.0) */
+} pga_paged_kv;
+
+/*
+ * Speculative-verify attention: 1..4 query tokens per sequence against that
+ * sequence's whole KV history (SGLang PR #36330, Motivation: short multi-token
+ * queries, 16 query heads per KV head, head size 256, page size 16, FP8 KV).
+ * All r * Lq_b query rows of one KV group are packed into one tile, so each KV
+ * page is loaded once for every speculative token of the group
+ * (Modifications: BLOCK_M = 16 x BLOCK_Q).  Long histories are cut into
+ * segments of kv_split_tokens keys whose fp32 partial results are merged by a
+ * separate log-sum-exp kernel (Modifications: 8-64 segments).
+ *
+ *   q             [T, num_q_heads, 256] bf16 (q_dtype must be PGA_DTYPE_BF16)
+ *   q_descale     device scalar or NULL; used as a factor on the scores
+ *   cu_seqlens_q  [num_seqs + 1] int32, non-decreasing, cu_seqlens_q[0] = 0
+ *   seq_lens_k    [num_seqs] int32, Lk_b >= Lq_b, including the new tokens
+ *   max_q_len     host upper bound of Lq_b, 1..4; (Hq / Hkv) * max_q_len <= 64
+ *   max_kv_len    host upper bound of Lk_b
+ *   kv_split_tokens  0 = library's choice; otherwise the segment length, a
+ *                 positive multiple of 64
+ *   workspace     device buffer of at least paged_attn_verify_workspace_bytes()
+ *                 (may be NULL when that size is 0)
+ *   out           [T, num_q_heads, 256] bf16;  lse  [T, num_q_heads] fp32 or NULL
+ * Returns PGA_OK or a PGA_ERR_* code.
+ */
+int paged_attn_verify(const void* q, int32_t q_dtype, const float* q_descale, int32_t num_q_heads,
+                      int32_t num_seqs, const int32_t* cu_seqlens_q, const int32_t* seq_lens_k,
+                      int32_t max_q_len, int32_t max_kv_len, const pga_paged_kv* kv, float softmax_scale,
+                      int32_t kv_split_tokens, void* workspace, size_t workspace_bytes, void* out, float* lse,
+                      void* stream);
+
+/* Workspace bytes paged_attn_verify needs for these host bounds (0 when no
+ * sequence can span more than one segment). */
+size_t paged_attn_verify_workspace_bytes(int32_t num_q_heads, int32_t num_kv_heads, int32_t num_seqs,
+                                         int32_t max_q_len, int32_t max_kv_len, int32_t kv_split_tokens);
+
+/* Segment length paged_attn_verify uses for these host bounds (after resolving
+ * kv_split_tokens = 0), or 0 for invalid bounds. */
+int32_t paged_attn_verify_split_tokens(int32_t num_q_heads, int32_t num_kv_heads, int32_t num_seqs,
+                                       int32_t max_q_len, int32_t max_kv_len, int32_t kv_split_tokens);
+
+/*
+ * Prefill of new tokens against a cached prefix (ROCm/ATOM PR #2534, FMHA
+ * commit message: the cached+new keys are longer than the queries and the
+ * causal mask is bottom-right aligned).  Keys are read from the pages in the
+ * kernel; no gather to contiguous memory happens first (ROCm/ATOM PR #2830,
+ * recipe commit).
+ *
+ *   q             [T, num_q_heads, 256], FP8 E4M3FN or bf16 (q_dtype)
+ *   cu_seqlens_q  [num_seqs + 1] int32 prefix sums of Lq_b
+ *   cu_seqlens_k  [num_seqs + 1] int32 prefix sums of Lk_b, Lk_b >= Lq_b
+ *   max_seqlen_q, max_seqlen_k  host upper bounds of Lq_b and Lk_b
+ *   out           [T, num_q_heads, 256] bf16;  lse  [T, num_q_heads] fp32 or NULL
+ * FP8 Q requires FP8 KV.  Returns PGA_OK or a PGA_ERR_* code.
+ */
+int paged_attn_prefill_prefix(const void* q, int32_t q_dtype, const float* q_descale, int32_t num_q_heads,
+                              int32_t num_seqs, const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                              int32_t max_seqlen_q, int32_t max_seqlen_k, const pga_paged_kv* kv,
+                              float softmax_scale, void* out, float* lse, void* stream);
+
+/*
+ * Selected-token attention (vLLM PR #62590, Overview and Earlier results: each
+ * query row attends its own list of selected tokens, 2,051 per row at head
+ * size 256, BF16 or FP8 K/V).  Row i of q (a token of the sequence given by
+ * cu_seqlens_q) attends the logical positions indices[i * index_stride + e],
+ * e < num_selected; entries outside [0, Lk_b) are padding and skipped.  One
+ * list serves every head of the row; no causal rule is applied beyond it.
+ *
+ *   q             [num_q_tokens, num_q_heads, 256] bf16
+ *   num_q_tokens  host copy of cu_seqlens_q[num_seqs]
+ *   seq_lens_k    [num_seqs] int32; block_table_stride must cover each Lk_b
+ *   indices       [num_q_tokens, index_stride] int32
+ *   num_selected  entries read per row, 0 <= num_selected <= index_stride
+ *   out           [num_q_tokens, num_q_heads, 256] bf16;  lse  [num_q_tokens, num_q_heads] fp32 or NULL
+ * The pool must hold fewer than 2^31 tokens (num_pages * page_size).
+ * Returns PGA_OK or a PGA_ERR_* code.
+ */
+int sparse_paged_attn(const void* q, int32_t q_dtype, const float* q_descale, int32_t num_q_heads,
+                      int32_t num_q_tokens, int32_t num_seqs, const int32_t* cu_seqlens_q, const int32_t* seq_lens_k,
+                      const int32_t* indices, int64_t index_stride, int32_t num_selected, const pga_paged_kv* kv,
+                      float softmax_scale, void* out, float* lse, void* stream);
+
+/* Human-readable text of a status code (static storage). */
+const char* pga_status_string(int status);
+
+/* PGA_ABI_VERSION of the loaded library. */
+int pga_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGED_GQA_H_ */

@@ -1,0 +1,298 @@
+// Host side of the C ABI declared in include/paged_gqa.h: argument checks,
+// split-KV planning and kernel launches.  Every host-checkable condition is
+// checked before the first launch, so a rejected call launches nothing.
+#include "paged_gqa.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <climits>
+#include <cmath>
+#include <cstdint>
+
+#include "pga_args.h"
+
+namespace {
+
+using pga::KvArgs;
+
+constexpr int kBF16 = PGA_DTYPE_BF16;
+constexpr int kFP8 = PGA_DTYPE_FP8_E4M3;
+constexpr int kHeadDim = PGA_HEAD_DIM;
+constexpr int kMaxRowsPerGroup = 64;   // query rows of one kv group a verify workgroup holds
+constexpr int kTileKeys = 64;          // keys per LDS tile of the causal kernel
+constexpr int kTargetUnits = 1024;     // verify: workgroups to aim for (4 per CU on 256 CUs)
+constexpr int kMinSplit = 512;         // verify: shortest automatic segment
+constexpr int kMaxAutoSegments = 64;
+constexpr int kMaxGridYZ = 65535;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+bool pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
+int ilog2(int64_t x) {
+  int s = 0;
+  while ((int64_t(1) << s) < x) ++s;
+  return s;
+}
+int elt_bytes(int dt) { return dt == kFP8 ? 1 : 2; }
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Checks of the KV descriptor shared by all calls.  `pages_per_seq` is the
+// number of block-table columns the call may read (-1: not host-checkable).
+int check_kv(const pga_paged_kv* kv, int32_t num_q_heads, int64_t pages_per_seq) {
+  if (!kv) return PGA_ERR_NULL;
+  if (!kv->k_cache || !kv->v_cache || !kv->block_table) return PGA_ERR_NULL;
+  if (kv->dtype != kBF16 && kv->dtype != kFP8) return PGA_ERR_DTYPE;
+  if (kv->head_dim != kHeadDim) return PGA_ERR_SHAPE;
+  if (kv->num_kv_heads <= 0 || num_q_heads <= 0 || num_q_heads % kv->num_kv_heads != 0) return PGA_ERR_SHAPE;
+  if (kv->num_kv_heads > kMaxGridYZ) return PGA_ERR_UNSUPPORTED;
+  if (kv->num_pages <= 0) return PGA_ERR_SHAPE;
+  if (!pow2(kv->page_size) || kv->page_size < 16 || kv->page_size > 1024) return PGA_ERR_UNSUPPORTED;
+  const int64_t per16 = 16 / elt_bytes(kv->dtype);  // elements in 16 bytes
+  const int64_t st[6] = {kv->k_stride_page, kv->k_stride_token, kv->k_stride_head,
+                         kv->v_stride_page, kv->v_stride_token, kv->v_stride_head};
+  for (int64_t s : st)
+    if (s < 0 || s % per16 != 0) return PGA_ERR_UNSUPPORTED;
+  if (!aligned(kv->k_cache, 16) || !aligned(kv->v_cache, 16)) return PGA_ERR_UNSUPPORTED;
+  if (kv->block_table_stride < 0 || (pages_per_seq > 0 && kv->block_table_stride < pages_per_seq))
+    return PGA_ERR_SHAPE;
+  return PGA_OK;
+}
+
+KvArgs make_kv(const pga_paged_kv* kv) {
+  const int64_t e = elt_bytes(kv->dtype);
+  KvArgs a;
+  a.k = static_cast<const uint8_t*>(kv->k_cache);
+  a.v = static_cast<const uint8_t*>(kv->v_cache);
+  a.k_sp = kv->k_stride_page * e;
+  a.k_st = kv->k_stride_token * e;
+  a.k_sh = kv->k_stride_head * e;
+  a.v_sp = kv->v_stride_page * e;
+  a.v_st = kv->v_stride_token * e;
+  a.v_sh = kv->v_stride_head * e;
+  a.bt = kv->block_table;
+  a.bt_stride = kv->block_table_stride;
+  a.page_size = kv->page_size;
+  a.page_shift = ilog2(kv->page_size);
+  a.num_pages = kv->num_pages;
+  a.num_kv_heads = kv->num_kv_heads;
+  a.k_ds = kv->k_descale;
+  a.v_ds = kv->v_descale;
+  return a;
+}
+
+// Segment length for verify (a multiple of the 64-key tile), or 0 if invalid.
+int32_t resolve_split(int32_t num_kv_heads, int32_t num_seqs, int32_t max_kv_len, int32_t kv_split_tokens) {
+  if (kv_split_tokens < 0 || kv_split_tokens % kTileKeys != 0) return 0;
+  if (kv_split_tokens > 0) return kv_split_tokens;
+  const int64_t units = std::max<int64_t>(1, int64_t(num_seqs) * num_kv_heads);
+  const int64_t nseg = std::min<int64_t>(kMaxAutoSegments, std::max<int64_t>(1, cdiv(kTargetUnits, units)));
+  int64_t split = cdiv(std::max<int32_t>(max_kv_len, 1), nseg);
+  split = cdiv(split, kTileKeys) * kTileKeys;
+  split = std::max<int64_t>(split, kMinSplit);
+  return static_cast<int32_t>(std::min<int64_t>(split, INT32_MAX / 2));
+}
+
+struct VerifyPlan {
+  int32_t split = 0, max_segs = 1, rows_cap = 0;
+  size_t ws_o_bytes = 0, ws_bytes = 0;
+};
+
+bool plan_verify(int32_t hq, int32_t hkv, int32_t num_seqs, int32_t max_q_len, int32_t max_kv_len,
+                 int32_t kv_split_tokens, VerifyPlan& p) {
+  if (hq <= 0 || hkv <= 0 || hq % hkv != 0 || num_seqs < 0 || max_q_len < 1 || max_kv_len < 0) return false;
+  p.split = resolve_split(hkv, num_seqs, max_kv_len, kv_split_tokens);
+  if (p.split <= 0) return false;
+  p.max_segs = static_cast<int32_t>(std::max<int64_t>(1, cdiv(max_kv_len, p.split)));
+  p.rows_cap = (hq / hkv) * max_q_len;
+  if (p.max_segs > 1) {
+    const size_t units = size_t(num_seqs) * hkv * p.max_segs;
+    p.ws_o_bytes = units * p.rows_cap * kHeadDim * sizeof(float);
+    p.ws_o_bytes = (p.ws_o_bytes + 255) & ~size_t(255);
+    p.ws_bytes = p.ws_o_bytes + units * p.rows_cap * sizeof(float);
+  }
+  return true;
+}
+
+int launch_status(hipError_t e) { return e == hipSuccess ? PGA_OK : PGA_ERR_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+int pga_abi_version(void) { return PGA_ABI_VERSION; }
+
+const char* pga_status_string(int status) {
+  switch (status) {
+    case PGA_OK: return "ok";
+    case PGA_ERR_NULL: return "a required pointer is NULL";
+    case PGA_ERR_SHAPE: return "invalid shape or length bound";
+    case PGA_ERR_DTYPE: return "unsupported dtype or dtype pair";
+    case PGA_ERR_UNSUPPORTED: return "outside the kernel envelope (page size, alignment, rows per kv group)";
+    case PGA_ERR_WORKSPACE: return "workspace too small";
+    case PGA_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+size_t paged_attn_verify_workspace_bytes(int32_t num_q_heads, int32_t num_kv_heads, int32_t num_seqs,
+                                         int32_t max_q_len, int32_t max_kv_len, int32_t kv_split_tokens) {
+  VerifyPlan p;
+  if (!plan_verify(num_q_heads, num_kv_heads, num_seqs, max_q_len, max_kv_len, kv_split_tokens, p)) return 0;
+  return p.ws_bytes;
+}
+
+int32_t paged_attn_verify_split_tokens(int32_t num_q_heads, int32_t num_kv_heads, int32_t num_seqs,
+                                       int32_t max_q_len, int32_t max_kv_len, int32_t kv_split_tokens) {
+  VerifyPlan p;
+  if (!plan_verify(num_q_heads, num_kv_heads, num_seqs, max_q_len, max_kv_len, kv_split_tokens, p)) return 0;
+  return p.split;
+}
+
+int paged_attn_verify(const void* q, int32_t q_dtype, const float* q_descale, int32_t num_q_heads, int32_t num_seqs,
+                      const int32_t* cu_seqlens_q, const int32_t* seq_lens_k, int32_t max_q_len, int32_t max_kv_len,
+                      const pga_paged_kv* kv, float softmax_scale, int32_t kv_split_tokens, void* workspace,
+                      size_t workspace_bytes, void* out, float* lse, void* stream) {
+  if (!q || !cu_seqlens_q || !seq_lens_k || !out || !kv) return PGA_ERR_NULL;
+  if (num_seqs < 0 || num_q_heads <= 0 || max_kv_len < 0) return PGA_ERR_SHAPE;
+  if (max_q_len < 1 || max_q_len > 4) return PGA_ERR_SHAPE;
+  if (q_dtype != kBF16) return PGA_ERR_DTYPE;
+  if (!std::isfinite(softmax_scale)) return PGA_ERR_SHAPE;
+  if (int e = check_kv(kv, num_q_heads, cdiv(max_kv_len, kv->page_size > 0 ? kv->page_size : 1))) return e;
+  const int32_t r = num_q_heads / kv->num_kv_heads;
+  if (int64_t(r) * max_q_len > kMaxRowsPerGroup) return PGA_ERR_UNSUPPORTED;
+  if (kv_split_tokens < 0 || kv_split_tokens % kTileKeys != 0) return PGA_ERR_SHAPE;
+  if (num_seqs > kMaxGridYZ) return PGA_ERR_UNSUPPORTED;
+  if (!aligned(q, 16) || !aligned(out, 8) || (lse && !aligned(lse, 4))) return PGA_ERR_UNSUPPORTED;
+  VerifyPlan p;
+  if (!plan_verify(num_q_heads, kv->num_kv_heads, num_seqs, max_q_len, max_kv_len, kv_split_tokens, p))
+    return PGA_ERR_SHAPE;
+  if (p.ws_bytes > 0 && (!workspace || workspace_bytes < p.ws_bytes)) return PGA_ERR_WORKSPACE;
+  if (p.ws_bytes > 0 && !aligned(workspace, 256)) return PGA_ERR_UNSUPPORTED;
+  if (num_seqs == 0 || max_kv_len == 0) return PGA_OK;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  pga::CausalArgs a{};
+  a.q = q;
+  a.q_ds = q_descale;
+  a.hq = num_q_heads;
+  a.r = r;
+  a.num_seqs = num_seqs;
+  a.cu_q = cu_seqlens_q;
+  a.lens_k = seq_lens_k;
+  a.cu_k = nullptr;
+  a.kv = make_kv(kv);
+  a.c2_base = softmax_scale * 1.4426950408889634f;
+  a.max_q_len = max_q_len;
+  a.max_kv_len = max_kv_len;
+  a.tile_tokens = max_q_len;
+  a.seg_len = p.split;
+  a.max_segs = p.max_segs;
+  a.rows_cap = p.rows_cap;
+  a.out = static_cast<uint16_t*>(out);
+  a.lse = lse;
+  a.ws_o = p.ws_bytes ? static_cast<float*>(workspace) : nullptr;
+  a.ws_lse = p.ws_bytes ? reinterpret_cast<float*>(static_cast<char*>(workspace) + p.ws_o_bytes) : nullptr;
+  if (int e = launch_status(pga::launch_causal(a, false, kBF16, kv->dtype, p.max_segs, kv->num_kv_heads, num_seqs, s)))
+    return e;
+  if (p.max_segs > 1) {
+    pga::MergeArgs m{};
+    m.hq = num_q_heads;
+    m.r = r;
+    m.hkv = kv->num_kv_heads;
+    m.num_seqs = num_seqs;
+    m.max_kv_len = max_kv_len;
+    m.cu_q = cu_seqlens_q;
+    m.lens_k = seq_lens_k;
+    m.seg_len = p.split;
+    m.max_segs = p.max_segs;
+    m.rows_cap = p.rows_cap;
+    m.ws_o = a.ws_o;
+    m.ws_lse = a.ws_lse;
+    m.out = a.out;
+    m.lse = lse;
+    return launch_status(pga::launch_merge(m, max_q_len, s));
+  }
+  return PGA_OK;
+}
+
+int paged_attn_prefill_prefix(const void* q, int32_t q_dtype, const float* q_descale, int32_t num_q_heads,
+                              int32_t num_seqs, const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                              int32_t max_seqlen_q, int32_t max_seqlen_k, const pga_paged_kv* kv,
+                              float softmax_scale, void* out, float* lse, void* stream) {
+  if (!q || !cu_seqlens_q || !cu_seqlens_k || !out || !kv) return PGA_ERR_NULL;
+  if (num_seqs < 0 || num_q_heads <= 0 || max_seqlen_q < 0 || max_seqlen_k < 0) return PGA_ERR_SHAPE;
+  if (q_dtype != kBF16 && q_dtype != kFP8) return PGA_ERR_DTYPE;
+  if (!std::isfinite(softmax_scale)) return PGA_ERR_SHAPE;
+  if (int e = check_kv(kv, num_q_heads, cdiv(max_seqlen_k, kv->page_size > 0 ? kv->page_size : 1))) return e;
+  if (q_dtype == kFP8 && kv->dtype != kFP8) return PGA_ERR_DTYPE;
+  const int32_t r = num_q_heads / kv->num_kv_heads;
+  if (r > kMaxRowsPerGroup) return PGA_ERR_UNSUPPORTED;
+  if (num_seqs > kMaxGridYZ) return PGA_ERR_UNSUPPORTED;
+  if (!aligned(q, 16) || !aligned(out, 8) || (lse && !aligned(lse, 4))) return PGA_ERR_UNSUPPORTED;
+  if (num_seqs == 0 || max_seqlen_q == 0) return PGA_OK;
+
+  const int32_t tile_tokens = kMaxRowsPerGroup / r;
+  const int64_t q_tiles = cdiv(max_seqlen_q, tile_tokens);
+  if (q_tiles > INT32_MAX) return PGA_ERR_UNSUPPORTED;
+  pga::CausalArgs a{};
+  a.q = q;
+  a.q_ds = q_descale;
+  a.hq = num_q_heads;
+  a.r = r;
+  a.num_seqs = num_seqs;
+  a.cu_q = cu_seqlens_q;
+  a.lens_k = nullptr;
+  a.cu_k = cu_seqlens_k;
+  a.kv = make_kv(kv);
+  a.c2_base = softmax_scale * 1.4426950408889634f;
+  a.max_q_len = max_seqlen_q;
+  a.max_kv_len = max_seqlen_k;
+  a.tile_tokens = tile_tokens;
+  a.seg_len = 0;
+  a.max_segs = 1;
+  a.rows_cap = 0;
+  a.out = static_cast<uint16_t*>(out);
+  a.lse = lse;
+  a.ws_o = nullptr;
+  a.ws_lse = nullptr;
+  return launch_status(pga::launch_causal(a, true, q_dtype, kv->dtype, static_cast<int>(q_tiles), kv->num_kv_heads,
+                                          num_seqs, static_cast<hipStream_t>(stream)));
+}
+
+int sparse_paged_attn(const void* q, int32_t q_dtype, const float* q_descale, int32_t num_q_heads,
+                      int32_t num_q_tokens, int32_t num_seqs, const int32_t* cu_seqlens_q, const int32_t* seq_lens_k,
+                      const int32_t* indices, int64_t index_stride, int32_t num_selected, const pga_paged_kv* kv,
+                      float softmax_scale, void* out, float* lse, void* stream) {
+  if (!q || !cu_seqlens_q || !seq_lens_k || !out || !kv) return PGA_ERR_NULL;
+  if (num_selected > 0 && !indices) return PGA_ERR_NULL;
+  if (num_seqs < 0 || num_q_heads <= 0 || num_q_tokens < 0 || num_selected < 0 || index_stride < num_selected)
+    return PGA_ERR_SHAPE;
+  if (num_q_tokens > 0 && num_seqs == 0) return PGA_ERR_SHAPE;
+  if (q_dtype != kBF16) return PGA_ERR_DTYPE;
+  if (!std::isfinite(softmax_scale)) return PGA_ERR_SHAPE;
+  if (int e = check_kv(kv, num_q_heads, -1)) return e;
+  if (int64_t(kv->num_pages) * kv->page_size > INT32_MAX) return PGA_ERR_UNSUPPORTED;
+  if (!aligned(q, 16) || !aligned(out, 8) || (lse && !aligned(lse, 4))) return PGA_ERR_UNSUPPORTED;
+  if (num_selected > 0 && !aligned(indices, 4)) return PGA_ERR_UNSUPPORTED;
+  if (num_q_tokens == 0) return PGA_OK;
+
+  pga::SparseArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.q_ds = q_descale;
+  a.hq = num_q_heads;
+  a.r = num_q_heads / kv->num_kv_heads;
+  a.num_seqs = num_seqs;
+  a.num_tokens = num_q_tokens;
+  a.cu_q = cu_seqlens_q;
+  a.lens_k = seq_lens_k;
+  a.idx = indices;
+  a.idx_stride = index_stride;
+  a.num_selected = num_selected;
+  a.kv = make_kv(kv);
+  a.c2_base = softmax_scale * 1.4426950408889634f;
+  a.out = static_cast<uint16_t*>(out);
+  a.lse = lse;
+  return launch_status(pga::launch_sparse(a, kv->dtype, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

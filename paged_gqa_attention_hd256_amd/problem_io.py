@@ -1,0 +1,97 @@
+"""Upload a host-side problem description to the GPU and run it.
+
+``to_device`` accepts any object with the attributes of a paged-attention
+problem (numpy arrays of raw bf16 / FP8 codes: ``q``, ``k_cache``,
+``v_cache``, ``block_table``, ``cu_seqlens_q``, ``seq_lens_k``, optional
+``indices``; scalars ``q_dtype``, ``kv_dtype``, descales, ``softmax_scale``,
+``mode``, ``kv_layout``, ``kv_split_tokens``).  It only moves data; the
+attention itself runs in the HIP library.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import Optional
+
+import numpy as np
+import torch
+
+from . import PagedKV, paged_attn_prefill_prefix, paged_attn_verify, sparse_paged_attn, verify_workspace_bytes
+
+
+def _codes_to_tensor(codes: np.ndarray, dtype: str, device) -> torch.Tensor:
+    t = torch.from_numpy(np.ascontiguousarray(codes))
+    if dtype == "bf16":
+        t = t.view(torch.int16).view(torch.bfloat16)
+    else:
+        t = t.view(torch.uint8).view(torch.float8_e4m3fn)
+    return t.to(device)
+
+
+def _scalar(x: float, device) -> torch.Tensor:
+    return torch.tensor([x], dtype=torch.float32, device=device)
+
+
+@dataclass
+class DeviceProblem:
+    mode: str
+    q: torch.Tensor
+    q_descale: Optional[torch.Tensor]
+    cu_seqlens_q: torch.Tensor
+    seq_lens_k: torch.Tensor
+    cu_seqlens_k: torch.Tensor
+    kv: PagedKV
+    softmax_scale: float
+    max_q_len: int
+    max_kv_len: int
+    kv_split_tokens: int
+    indices: Optional[torch.Tensor]
+    out: torch.Tensor
+    lse: torch.Tensor
+    workspace: Optional[torch.Tensor]
+
+
+def to_device(p, device="cuda", kv_split_tokens: Optional[int] = None) -> DeviceProblem:
+    q = _codes_to_tensor(p.q, p.q_dtype, device)
+    k = _codes_to_tensor(p.k_cache, p.kv_dtype, device)
+    v = _codes_to_tensor(p.v_cache, p.kv_dtype, device)
+    bt = torch.from_numpy(np.ascontiguousarray(p.block_table, dtype=np.int32)).to(device)
+    kv = PagedKV(k, v, bt, layout=p.kv_layout, k_descale=_scalar(p.k_descale, device),
+                 v_descale=_scalar(p.v_descale, device))
+    cu_q = torch.from_numpy(np.ascontiguousarray(p.cu_seqlens_q, dtype=np.int32)).to(device)
+    lens_k = torch.from_numpy(np.ascontiguousarray(p.seq_lens_k, dtype=np.int32)).to(device)
+    cu_k_np = np.zeros(len(p.seq_lens_k) + 1, dtype=np.int32)
+    cu_k_np[1:] = np.cumsum(p.seq_lens_k)
+    cu_k = torch.from_numpy(cu_k_np).to(device)
+    idx = None
+    if getattr(p, "indices", None) is not None:
+        idx = torch.from_numpy(np.ascontiguousarray(p.indices, dtype=np.int32)).to(device)
+    T, Hq = p.q.shape[0], p.q.shape[1]
+    out = torch.empty((T, Hq, 256), dtype=torch.bfloat16, device=device)
+    lse = torch.empty((T, Hq), dtype=torch.float32, device=device)
+    max_q = int(np.diff(p.cu_seqlens_q).max()) if len(p.seq_lens_k) else 0
+    max_k = int(np.max(p.seq_lens_k)) if len(p.seq_lens_k) else 0
+    split = p.kv_split_tokens if kv_split_tokens is None else kv_split_tokens
+    ws = None
+    if p.mode == "verify":
+        need = verify_workspace_bytes(Hq, kv.num_kv_heads, len(p.seq_lens_k), max(1, max_q), max_k, split)
+        if need:
+            ws = torch.empty(need, dtype=torch.uint8, device=device)
+    q_ds = _scalar(p.q_descale, device) if p.q_dtype != "bf16" else None
+    return DeviceProblem(p.mode, q, q_ds, cu_q, lens_k, cu_k, kv, float(p.softmax_scale), max_q, max_k, split, idx,
+                         out, lse, ws)
+
+
+def run(dp: DeviceProblem, stream=None) -> torch.Tensor:
+    """One call of the entry point matching ``dp.mode``; writes dp.out / dp.lse."""
+    if dp.mode == "verify":
+        return paged_attn_verify(dp.q, dp.cu_seqlens_q, dp.seq_lens_k, dp.max_q_len, dp.max_kv_len, dp.kv,
+                                 dp.softmax_scale, dp.kv_split_tokens, q_descale=dp.q_descale, workspace=dp.workspace,
+                                 out=dp.out, lse=dp.lse, stream=stream)
+    if dp.mode == "prefill":
+        return paged_attn_prefill_prefix(dp.q, dp.cu_seqlens_q, dp.cu_seqlens_k, dp.max_q_len, dp.max_kv_len, dp.kv,
+                                         dp.softmax_scale, q_descale=dp.q_descale, out=dp.out, lse=dp.lse,
+                                         stream=stream)
+    if dp.mode == "sparse":
+        return sparse_paged_attn(dp.q, dp.cu_seqlens_q, dp.seq_lens_k, dp.indices, dp.kv, dp.softmax_scale,
+                                 q_descale=dp.q_descale, out=dp.out, lse=dp.lse, stream=stream)
+    raise ValueError(dp.mode)

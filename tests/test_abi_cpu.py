@@ -1,0 +1,163 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/paged_gqa.h declares, and rejects invalid arguments with the
+documented status codes before anything is launched (argument checks never
+dereference device pointers, so host placeholders stand in for them)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import paged_gqa_attention_hd256_amd as pga
+from paged_gqa_attention_hd256_amd import _KV
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "paged_gqa.h")
+
+OK, ENULL, ESHAPE, EDTYPE, EUNSUP, EWS = 0, 1, 2, 3, 4, 5
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^[A-Za-z_][\w \*]*?\b([a-z_][a-z0-9_]*)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(pga.library_path()):
+        from paged_gqa_attention_hd256_amd import build
+        build.build(verbose=False)
+    return pga.load_library()
+
+
+def test_library_exports_every_declared_function(lib):
+    names = declared_functions()
+    assert {"paged_attn_verify", "paged_attn_prefill_prefix", "sparse_paged_attn"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert lib.pga_abi_version() == 1
+
+
+def test_status_strings(lib):
+    for code in range(0, 7):
+        assert pga.status_string(code)
+    assert pga.status_string(99) == "unknown status"
+
+
+# Host buffers stand in for device memory: validation never dereferences them.
+_buf = ctypes.create_string_buffer(1 << 16)
+_base = (ctypes.addressof(_buf) + 255) & ~255
+
+
+def P(off=0):
+    return _base + off
+
+
+def kv_struct(**over):
+    s = _KV()
+    s.k_cache, s.v_cache = P(0), P(4096)
+    s.dtype, s.num_kv_heads, s.head_dim, s.page_size, s.num_pages = 2, 1, 256, 16, 128
+    s.k_stride_page, s.k_stride_token, s.k_stride_head = 16 * 256, 256, 256
+    s.v_stride_page, s.v_stride_token, s.v_stride_head = 16 * 256, 256, 256
+    s.block_table, s.block_table_stride = P(8192), 64
+    s.k_descale = s.v_descale = None
+    for k, v in over.items():
+        setattr(s, k, v)
+    return s
+
+
+def verify(lib, kv=None, **kw):
+    a = dict(q=P(), q_dtype=1, qds=None, hq=16, nseq=2, cuq=P(16384), lk=P(16384 + 64), maxq=4, maxk=1000,
+             scale=0.0625, split=0, ws=None, wsb=0, out=P(20000), lse=None)
+    a.update(kw)
+    kv = kv or kv_struct()
+    return lib.paged_attn_verify(a["q"], a["q_dtype"], a["qds"], a["hq"], a["nseq"], a["cuq"], a["lk"], a["maxq"],
+                                 a["maxk"], ctypes.byref(kv), a["scale"], a["split"], a["ws"], a["wsb"], a["out"],
+                                 a["lse"], None)
+
+
+def test_verify_rejects_invalid_arguments(lib):
+    assert verify(lib, q=None) == ENULL
+    assert verify(lib, out=None) == ENULL
+    assert verify(lib, kv=kv_struct(block_table=None)) == ENULL
+    assert verify(lib, q_dtype=2) == EDTYPE
+    assert verify(lib, kv=kv_struct(dtype=7)) == EDTYPE
+    assert verify(lib, kv=kv_struct(head_dim=128)) == ESHAPE
+    assert verify(lib, kv=kv_struct(num_kv_heads=2), hq=15) == ESHAPE
+    assert verify(lib, maxq=0) == ESHAPE
+    assert verify(lib, maxq=5) == ESHAPE
+    assert verify(lib, hq=32) == EUNSUP                     # 32 x 4 rows > 64
+    assert verify(lib, nseq=-1) == ESHAPE
+    assert verify(lib, maxk=-1) == ESHAPE
+    assert verify(lib, split=100) == ESHAPE                 # not a multiple of 64
+    assert verify(lib, kv=kv_struct(page_size=24)) == EUNSUP
+    assert verify(lib, kv=kv_struct(page_size=8)) == EUNSUP
+    assert verify(lib, kv=kv_struct(k_stride_token=250)) == EUNSUP
+    assert verify(lib, kv=kv_struct(k_cache=P(8))) == EUNSUP   # misaligned pool
+    assert verify(lib, q=P(4)) == EUNSUP
+    assert verify(lib, kv=kv_struct(block_table_stride=10)) == ESHAPE  # < ceil(1000 / 16)
+    assert verify(lib, scale=float("nan")) == ESHAPE
+    need = pga.verify_workspace_bytes(16, 1, 2, 4, 1000, 0)
+    assert need > 0
+    assert verify(lib, ws=None, wsb=0) == EWS
+    assert verify(lib, ws=P(), wsb=need - 1) == EWS
+
+
+def test_verify_nothing_to_do_returns_ok_without_launch(lib):
+    assert verify(lib, nseq=0) == OK
+    assert verify(lib, maxk=0) == OK
+
+
+def test_verify_workspace_plan(lib):
+    # One segment: no workspace.  Split segments: fp32 partial rows plus one lse per row.
+    assert pga.verify_workspace_bytes(16, 1, 64, 4, 4096, 1 << 20) == 0
+    split = pga.verify_split_tokens(16, 1, 64, 4, 32768, 0)
+    assert split % 64 == 0 and split >= 512
+    segs = -(-32768 // split)
+    b = pga.verify_workspace_bytes(16, 1, 64, 4, 32768, 0)
+    o = 64 * segs * 64 * 256 * 4
+    assert b == ((o + 255) & ~255) + 64 * segs * 64 * 4
+    assert pga.verify_split_tokens(32, 2, 128, 3, 65536, 4096) == 4096
+    assert pga.verify_workspace_bytes(16, 1, 2, 4, 1000, 100) == 0   # invalid split -> 0
+
+
+def prefill(lib, kv=None, **kw):
+    a = dict(q=P(), q_dtype=2, qds=None, hq=8, nseq=1, cuq=P(16384), cuk=P(16384 + 64), maxq=100, maxk=300,
+             scale=0.0625, out=P(20000), lse=None)
+    a.update(kw)
+    kv = kv or kv_struct()
+    return lib.paged_attn_prefill_prefix(a["q"], a["q_dtype"], a["qds"], a["hq"], a["nseq"], a["cuq"], a["cuk"],
+                                         a["maxq"], a["maxk"], ctypes.byref(kv), a["scale"], a["out"], a["lse"], None)
+
+
+def test_prefill_rejects_invalid_arguments(lib):
+    assert prefill(lib, cuk=None) == ENULL
+    assert prefill(lib, q_dtype=3) == EDTYPE
+    assert prefill(lib, kv=kv_struct(dtype=1)) == EDTYPE      # FP8 Q needs FP8 KV
+    assert prefill(lib, hq=128) == EUNSUP                     # 128 query heads per kv head
+    assert prefill(lib, maxq=-1) == ESHAPE
+    assert prefill(lib, kv=kv_struct(block_table_stride=5)) == ESHAPE
+    assert prefill(lib, nseq=0) == OK
+    assert prefill(lib, maxq=0) == OK
+
+
+def sparse(lib, kv=None, **kw):
+    a = dict(q=P(), q_dtype=1, qds=None, hq=24, ntok=8, nseq=1, cuq=P(16384), lk=P(16384 + 64), idx=P(30000),
+             stride=64, nsel=64, scale=0.0625, out=P(20000), lse=None)
+    a.update(kw)
+    kv = kv or kv_struct(num_kv_heads=2)
+    return lib.sparse_paged_attn(a["q"], a["q_dtype"], a["qds"], a["hq"], a["ntok"], a["nseq"], a["cuq"], a["lk"],
+                                 a["idx"], a["stride"], a["nsel"], ctypes.byref(kv), a["scale"], a["out"], a["lse"],
+                                 None)
+
+
+def test_sparse_rejects_invalid_arguments(lib):
+    assert sparse(lib, idx=None) == ENULL
+    assert sparse(lib, q_dtype=2) == EDTYPE
+    assert sparse(lib, stride=10) == ESHAPE                   # fewer columns than num_selected
+    assert sparse(lib, nsel=-1) == ESHAPE
+    assert sparse(lib, nseq=0) == ESHAPE                      # rows without a sequence
+    assert sparse(lib, hq=25) == ESHAPE
+    assert sparse(lib, kv=kv_struct(num_kv_heads=2, num_pages=1 << 30, page_size=64)) == EUNSUP
+    assert sparse(lib, ntok=0) == OK

@@ -1,0 +1,164 @@
+"""GPU parity: the HIP library against the fp64 oracle, element by element.
+
+Bar: max-abs <= 1e-2 and rel-L2 <= 2e-3 over the bf16 output, lse within
+1e-3, no NaN/Inf; bitwise run-to-run determinism and bitwise invariance to
+the physical page permutation.  Cases span several 64-key tiles with ragged
+tails, split and unsplit verify, both pool layouts, page sizes 16 and 64,
+NaN-poisoned pools (any read outside the visible set shows up), and the
+degenerate shapes of each call.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import workloads as w
+from tests import refs
+from tests.gpu_util import assert_parity, bf16_bits_to_f64, run_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+def _check(p, split=None, what=None):
+    print(f"case {p.name} split={split}", flush=True)
+    ref, ref_lse = oracle.attention(p)
+    bits, lse = run_gpu(p, split=split)
+    return assert_parity(bits, lse, ref, ref_lse, what=what or p.name)
+
+
+# ------------------------------------------------------------------ verify ---
+VERIFY_CASES = [
+    ("bf16_q2_16to1", dict(seed=[11], lq=[2, 2], lk=[600, 1000], hq=16, hkv=1, kv=w.BF16)),
+    ("fp8_q4_16to1_tails", dict(seed=[12], lq=[4, 4, 4, 4], lk=[65, 1023, 1217, 4], hq=16, hkv=1, kv=w.FP8)),
+    ("fp8_q3_32to2", dict(seed=[13], lq=[3, 3, 3], lk=[513, 130, 2049], hq=32, hkv=2, kv=w.FP8)),
+    ("fp8_varlen_q", dict(seed=[14], lq=[1, 2, 3, 4], lk=[300, 77, 1500, 640], hq=16, hkv=1, kv=w.FP8)),
+    ("bf16_q4_8to1", dict(seed=[15], lq=[4, 4], lk=[200, 333], hq=8, hkv=1, kv=w.BF16)),
+    ("fp8_q4_12to1", dict(seed=[16], lq=[4, 2], lk=[400, 129], hq=12, hkv=1, kv=w.FP8)),
+    ("fp8_q1_64to1", dict(seed=[17], lq=[1, 1], lk=[700, 64], hq=64, hkv=1, kv=w.FP8)),
+    ("bf16_hnd_page64", dict(seed=[18], lq=[2, 3], lk=[500, 901], hq=16, hkv=2, kv=w.BF16, layout="HND", page=64)),
+    ("fp8_nhd_page64", dict(seed=[19], lq=[4], lk=[1300], hq=16, hkv=1, kv=w.FP8, page=64)),
+    ("fp8_lk_equals_lq", dict(seed=[20], lq=[4, 1, 3], lk=[4, 1, 3], hq=16, hkv=1, kv=w.FP8)),
+]
+
+
+def _verify_problem(name, c, poison=False):
+    p = w.make_causal(name, c["seed"], c["lq"], c["lk"], c["hq"], c["hkv"], kv_dtype=c["kv"],
+                      page_size=c.get("page", 16), layout=c.get("layout", "NHD"),
+                      kv_sigma=0.5 if c["kv"] == w.FP8 else 1.0, mode="verify")
+    return w.poison_unused(p) if poison else p
+
+
+@pytest.mark.parametrize("name,c", VERIFY_CASES, ids=[n for n, _ in VERIFY_CASES])
+@pytest.mark.parametrize("split", [0, 64, 256, 1 << 20])
+def test_verify_parity(name, c, split):
+    p = _verify_problem(name, c, poison=True)
+    _check(p, split=split, what=f"{name}/split{split}")
+
+
+def test_verify_tiny_config_full():
+    # The tiny verify workload exactly: 2 sequences, q_len 2, 16:1, BF16, 128-page pool.
+    p = w.poison_unused(w.config("tiny_verify"))
+    for split in (0, 64, 4096):
+        _check(p, split=split, what=f"tiny_verify/split{split}")
+
+
+def test_verify_zero_query_tokens_in_batch():
+    # A sequence with no query tokens contributes no rows and must not disturb the others.
+    p = w.make_causal("zero_q", [21], [2, 0, 3], [100, 50, 300], 16, 1, kv_dtype=w.FP8, kv_sigma=0.5)
+    _check(w.poison_unused(p), split=64)
+
+
+# ----------------------------------------------------------------- prefill ---
+PREFILL_CASES = [
+    ("fp8_prefix", dict(seed=[31], lq=[100], lk=[300], hq=8, hkv=1, q=w.FP8, kv=w.FP8)),
+    ("fp8_varlen", dict(seed=[32], lq=[37, 64, 5], lk=[87, 264, 5], hq=8, hkv=1, q=w.FP8, kv=w.FP8)),
+    ("bf16q_fp8kv", dict(seed=[33], lq=[50], lk=[181], hq=16, hkv=2, q=w.BF16, kv=w.FP8)),
+    ("bf16_bf16", dict(seed=[34], lq=[70, 3], lk=[70, 200], hq=8, hkv=1, q=w.BF16, kv=w.BF16)),
+    ("fp8_hnd_page64", dict(seed=[35], lq=[65], lk=[390], hq=8, hkv=1, q=w.FP8, kv=w.FP8, layout="HND", page=64)),
+    ("fp8_pure_causal", dict(seed=[36], lq=[129], lk=[129], hq=8, hkv=1, q=w.FP8, kv=w.FP8)),
+]
+
+
+@pytest.mark.parametrize("name,c", PREFILL_CASES, ids=[n for n, _ in PREFILL_CASES])
+def test_prefill_parity(name, c):
+    p = w.make_causal(name, c["seed"], c["lq"], c["lk"], c["hq"], c["hkv"], kv_dtype=c["kv"], q_dtype=c["q"],
+                      page_size=c.get("page", 16), layout=c.get("layout", "NHD"), mode="prefill")
+    _check(w.poison_unused(p))
+
+
+# ------------------------------------------------------------------ sparse ---
+SPARSE_CASES = [
+    ("bf16_24to2", dict(seed=[41], lq=[40], lk=[2000], hq=24, hkv=2, n=300, kv=w.BF16, width=320)),
+    ("fp8_24to2", dict(seed=[42], lq=[40], lk=[2000], hq=24, hkv=2, n=300, kv=w.FP8, width=320)),
+    ("fp8_two_chunks", dict(seed=[43], lq=[6], lk=[4000], hq=24, hkv=2, n=1500, kv=w.FP8)),
+    ("bf16_multi_seq", dict(seed=[44], lq=[5, 9, 3], lk=[700, 90, 1200], hq=12, hkv=1, n=200, kv=w.BF16)),
+    ("fp8_16to1", dict(seed=[45], lq=[10], lk=[999], hq=16, hkv=1, n=257, kv=w.FP8)),
+    ("bf16_32to1", dict(seed=[46], lq=[7], lk=[1500], hq=32, hkv=1, n=100, kv=w.BF16)),
+    ("fp8_hnd_page64", dict(seed=[47], lq=[8], lk=[3000], hq=6, hkv=1, n=400, kv=w.FP8, layout="HND", page=64)),
+]
+
+
+def _sparse_problem(name, c, pad=0.0):
+    return w.make_sparse(name, c["seed"], c["lq"], c["lk"], c["hq"], c["hkv"], c["n"], kv_dtype=c["kv"],
+                         page_size=c.get("page", 16), layout=c.get("layout", "NHD"), width=c.get("width"),
+                         pad_fraction=pad)
+
+
+@pytest.mark.parametrize("name,c", SPARSE_CASES, ids=[n for n, _ in SPARSE_CASES])
+@pytest.mark.parametrize("pad", [0.0, 0.25])
+def test_sparse_parity(name, c, pad):
+    p = w.poison_unused(_sparse_problem(name, c, pad))
+    _check(p, what=f"{name}/pad{pad}")
+
+
+def test_sparse_out_of_range_entries_are_padding():
+    p = _sparse_problem("oor", dict(seed=[48], lq=[8], lk=[500], hq=24, hkv=2, n=64, kv=w.BF16, width=80))
+    base_bits, _ = run_gpu(p)
+    q = _sparse_problem("oor", dict(seed=[48], lq=[8], lk=[500], hq=24, hkv=2, n=64, kv=w.BF16, width=80))
+    pad = q.indices < 0
+    q.indices[pad] = 500 + (np.arange(pad.sum()) % 3) * 12345  # >= Lk: also padding
+    bits, _ = run_gpu(q)
+    assert np.array_equal(bits, base_bits)
+    q.indices[3, :] = -1  # an all-padding row: out = 0, lse = -inf
+    bits, lse = run_gpu(q)
+    assert np.all(bf16_bits_to_f64(bits[3]) == 0) and np.all(np.isneginf(lse[3]))
+
+
+@pytest.mark.parametrize("kv_dtype", [w.BF16, w.FP8])
+def test_sparse_index_handling_bit_exact(kv_dtype):
+    """A single selected index must give RNE(v_ds * V_j) bitwise; q = 0 with two
+    indices must give RNE(v_ds * (V_a + V_b) / 2) bitwise."""
+    p = w.make_sparse("one", [49], [16], [800], 24, 2, 1, kv_dtype=kv_dtype)
+    if kv_dtype == w.FP8:
+        p.v_descale = 0.25  # a power of two keeps v_ds * V exact before the final rounding
+    bits, _ = run_gpu(p)
+    _, v = refs.logical_kv(p, 0)
+    for t in range(16):
+        j = p.indices[t, 0]
+        expect = refs.bf16_round(np.repeat(v[j].numpy(), 12, axis=0))  # [24, 256]
+        assert np.array_equal(bf16_bits_to_f64(bits[t]), expect)
+    two = w.make_sparse("two", [50], [16], [800], 24, 2, 2, kv_dtype=kv_dtype)
+    if kv_dtype == w.FP8:
+        two.v_descale = 0.25
+    two.q[:] = 0
+    bits, _ = run_gpu(two)
+    _, v = refs.logical_kv(two, 0)
+    for t in range(16):
+        a, b = two.indices[t, :2]
+        expect = refs.bf16_round(np.repeat(((v[a] + v[b]) / 2).numpy(), 12, axis=0))
+        assert np.array_equal(bf16_bits_to_f64(bits[t]), expect)
+
+
+# --------------------------------------------------- determinism, permutation ---
+@pytest.mark.parametrize("mode", ["verify", "prefill", "sparse"])
+def test_bitwise_determinism_and_page_permutation_invariance(mode):
+    if mode == "sparse":
+        p = _sparse_problem("det", dict(seed=[61], lq=[12], lk=[1800], hq=24, hkv=2, n=333, kv=w.FP8))
+    else:
+        p = w.make_causal("det", [62], [4, 3], [1500, 700], 16, 1, kv_dtype=w.FP8, kv_sigma=0.5,
+                          q_dtype=w.FP8 if mode == "prefill" else w.BF16, mode=mode)
+    runs = run_gpu(p, split=256 if mode == "verify" else None, repeat=10)
+    for bits, lse in runs[1:]:
+        assert np.array_equal(bits, runs[0][0]) and np.array_equal(lse, runs[0][1], equal_nan=True)
+    q = refs.repack(p, 5, "NHD", extra_pages=7, fill_code=w.NAN_CODE[p.kv_dtype])
+    bits, lse = run_gpu(q, split=256 if mode == "verify" else None)
+    assert np.array_equal(bits, runs[0][0])
