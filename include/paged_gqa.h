@@ -129,6 +129,24 @@ int paged_attn_verify(const void* q, int32_t q_dtype, const float* q_descale, in
                       int32_t kv_split_tokens, void* workspace, size_t workspace_bytes, void* out, float* lse,
                       void* stream);
 
+/* The two stages of paged_attn_verify, callable on their own with the same
+ * arguments: the attention kernel over every (segment, kv head, sequence),
+ * which writes the final output of single-segment sequences and fp32 partial
+ * outputs plus lse values to the workspace for the others; then the
+ * log-sum-exp merge of those partials.  paged_attn_verify is exactly stage 1
+ * followed by stage 2 on the same stream.  A caller that shards a sequence's
+ * segments across devices can gather the workspace partials and run stage 2. */
+int paged_attn_verify_partials(const void* q, int32_t q_dtype, const float* q_descale, int32_t num_q_heads,
+                               int32_t num_seqs, const int32_t* cu_seqlens_q, const int32_t* seq_lens_k,
+                               int32_t max_q_len, int32_t max_kv_len, const pga_paged_kv* kv, float softmax_scale,
+                               int32_t kv_split_tokens, void* workspace, size_t workspace_bytes, void* out,
+                               float* lse, void* stream);
+int paged_attn_verify_merge(const void* q, int32_t q_dtype, const float* q_descale, int32_t num_q_heads,
+                            int32_t num_seqs, const int32_t* cu_seqlens_q, const int32_t* seq_lens_k,
+                            int32_t max_q_len, int32_t max_kv_len, const pga_paged_kv* kv, float softmax_scale,
+                            int32_t kv_split_tokens, void* workspace, size_t workspace_bytes, void* out,
+                            float* lse, void* stream);
+
 /* Workspace bytes paged_attn_verify needs for these host bounds (0 when no
  * sequence can span more than one segment). */
 size_t paged_attn_verify_workspace_bytes(int32_t num_q_heads, int32_t num_kv_heads, int32_t num_seqs,

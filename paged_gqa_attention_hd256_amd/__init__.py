@@ -71,8 +71,9 @@ def load_library():
             lib = ctypes.CDLL(_SO)
             P, I32, I64, SZ, F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
             KVP = ctypes.POINTER(_KV)
-            lib.paged_attn_verify.argtypes = [P, I32, P, I32, I32, P, P, I32, I32, KVP, F, I32, P, SZ, P, P, P]
-            lib.paged_attn_verify.restype = ctypes.c_int
+            for fn in ("paged_attn_verify", "paged_attn_verify_partials", "paged_attn_verify_merge"):
+                getattr(lib, fn).argtypes = [P, I32, P, I32, I32, P, P, I32, I32, KVP, F, I32, P, SZ, P, P, P]
+                getattr(lib, fn).restype = ctypes.c_int
             lib.paged_attn_verify_workspace_bytes.argtypes = [I32, I32, I32, I32, I32, I32]
             lib.paged_attn_verify_workspace_bytes.restype = SZ
             lib.paged_attn_verify_split_tokens.argtypes = [I32, I32, I32, I32, I32, I32]
@@ -186,23 +187,30 @@ def _out(q: torch.Tensor, out):
     return out
 
 
+_VERIFY_STAGE = {"all": "paged_attn_verify", "partials": "paged_attn_verify_partials",
+                 "merge": "paged_attn_verify_merge"}
+
+
 def paged_attn_verify(q, cu_seqlens_q, seq_lens_k, max_q_len: int, max_kv_len: int, kv: PagedKV,
                       softmax_scale: float, kv_split_tokens: int = 0, q_descale=None, workspace=None,
-                      out=None, lse=None, stream=None):
-    """Speculative-verify attention; returns ``out`` ([T, Hq, 256] bf16)."""
+                      out=None, lse=None, stream=None, stage: str = "all"):
+    """Speculative-verify attention; returns ``out`` ([T, Hq, 256] bf16).
+    ``stage`` selects both kernels ("all"), only the attention kernel
+    ("partials") or only the log-sum-exp merge ("merge")."""
     lib = load_library()
+    fn = _VERIFY_STAGE[stage]
     hq = q.shape[1]
     need = verify_workspace_bytes(hq, kv.num_kv_heads, seq_lens_k.shape[0], max_q_len, max_kv_len, kv_split_tokens)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     out = _out(q, out)
     s = kv._struct()
-    st = lib.paged_attn_verify(q.data_ptr(), _dtype_code(q), _ptr(q_descale), hq, seq_lens_k.shape[0],
+    st = getattr(lib, fn)(q.data_ptr(), _dtype_code(q), _ptr(q_descale), hq, seq_lens_k.shape[0],
                                cu_seqlens_q.data_ptr(), seq_lens_k.data_ptr(), max_q_len, max_kv_len,
                                ctypes.byref(s), float(softmax_scale), kv_split_tokens, _ptr(workspace),
                                0 if workspace is None else workspace.numel() * workspace.element_size(),
                                out.data_ptr(), _ptr(lse), _stream(stream))
-    _check("paged_attn_verify", st)
+    _check(fn, st)
     return out
 
 

@@ -148,10 +148,13 @@ int32_t paged_attn_verify_split_tokens(int32_t num_q_heads, int32_t num_kv_heads
   return p.split;
 }
 
-int paged_attn_verify(const void* q, int32_t q_dtype, const float* q_descale, int32_t num_q_heads, int32_t num_seqs,
-                      const int32_t* cu_seqlens_q, const int32_t* seq_lens_k, int32_t max_q_len, int32_t max_kv_len,
-                      const pga_paged_kv* kv, float softmax_scale, int32_t kv_split_tokens, void* workspace,
-                      size_t workspace_bytes, void* out, float* lse, void* stream) {
+// Validates a verify call and fills the launch arguments; returns a status.
+static int prepare_verify(const void* q, int32_t q_dtype, const float* q_descale, int32_t num_q_heads,
+                          int32_t num_seqs, const int32_t* cu_seqlens_q, const int32_t* seq_lens_k, int32_t max_q_len,
+                          int32_t max_kv_len, const pga_paged_kv* kv, float softmax_scale, int32_t kv_split_tokens,
+                          void* workspace, size_t workspace_bytes, void* out, float* lse, VerifyPlan& p,
+                          pga::CausalArgs& a, pga::MergeArgs& m, bool& nothing) {
+  nothing = false;
   if (!q || !cu_seqlens_q || !seq_lens_k || !out || !kv) return PGA_ERR_NULL;
   if (num_seqs < 0 || num_q_heads <= 0 || max_kv_len < 0) return PGA_ERR_SHAPE;
   if (max_q_len < 1 || max_q_len > 4) return PGA_ERR_SHAPE;
@@ -163,15 +166,15 @@ int paged_attn_verify(const void* q, int32_t q_dtype, const float* q_descale, in
   if (kv_split_tokens < 0 || kv_split_tokens % kTileKeys != 0) return PGA_ERR_SHAPE;
   if (num_seqs > kMaxGridYZ) return PGA_ERR_UNSUPPORTED;
   if (!aligned(q, 16) || !aligned(out, 8) || (lse && !aligned(lse, 4))) return PGA_ERR_UNSUPPORTED;
-  VerifyPlan p;
   if (!plan_verify(num_q_heads, kv->num_kv_heads, num_seqs, max_q_len, max_kv_len, kv_split_tokens, p))
     return PGA_ERR_SHAPE;
   if (p.ws_bytes > 0 && (!workspace || workspace_bytes < p.ws_bytes)) return PGA_ERR_WORKSPACE;
   if (p.ws_bytes > 0 && !aligned(workspace, 256)) return PGA_ERR_UNSUPPORTED;
-  if (num_seqs == 0 || max_kv_len == 0) return PGA_OK;
-
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  pga::CausalArgs a{};
+  if (num_seqs == 0 || max_kv_len == 0) {
+    nothing = true;
+    return PGA_OK;
+  }
+  a = pga::CausalArgs{};
   a.q = q;
   a.q_ds = q_descale;
   a.hq = num_q_heads;
@@ -192,26 +195,71 @@ int paged_attn_verify(const void* q, int32_t q_dtype, const float* q_descale, in
   a.lse = lse;
   a.ws_o = p.ws_bytes ? static_cast<float*>(workspace) : nullptr;
   a.ws_lse = p.ws_bytes ? reinterpret_cast<float*>(static_cast<char*>(workspace) + p.ws_o_bytes) : nullptr;
+  m = pga::MergeArgs{};
+  m.hq = num_q_heads;
+  m.r = r;
+  m.hkv = kv->num_kv_heads;
+  m.num_seqs = num_seqs;
+  m.max_kv_len = max_kv_len;
+  m.cu_q = cu_seqlens_q;
+  m.lens_k = seq_lens_k;
+  m.seg_len = p.split;
+  m.max_segs = p.max_segs;
+  m.rows_cap = p.rows_cap;
+  m.ws_o = a.ws_o;
+  m.ws_lse = a.ws_lse;
+  m.out = a.out;
+  m.lse = lse;
+  return PGA_OK;
+}
+
+#define PGA_VERIFY_ARGS                                                                                       \
+  q, q_dtype, q_descale, num_q_heads, num_seqs, cu_seqlens_q, seq_lens_k, max_q_len, max_kv_len, kv,          \
+      softmax_scale, kv_split_tokens, workspace, workspace_bytes, out, lse
+
+int paged_attn_verify_partials(const void* q, int32_t q_dtype, const float* q_descale, int32_t num_q_heads,
+                               int32_t num_seqs, const int32_t* cu_seqlens_q, const int32_t* seq_lens_k,
+                               int32_t max_q_len, int32_t max_kv_len, const pga_paged_kv* kv, float softmax_scale,
+                               int32_t kv_split_tokens, void* workspace, size_t workspace_bytes, void* out,
+                               float* lse, void* stream) {
+  VerifyPlan p;
+  pga::CausalArgs a;
+  pga::MergeArgs m;
+  bool nothing;
+  if (int e = prepare_verify(PGA_VERIFY_ARGS, p, a, m, nothing)) return e;
+  if (nothing) return PGA_OK;
+  return launch_status(pga::launch_causal(a, false, kBF16, kv->dtype, p.max_segs, kv->num_kv_heads, num_seqs,
+                                          static_cast<hipStream_t>(stream)));
+}
+
+int paged_attn_verify_merge(const void* q, int32_t q_dtype, const float* q_descale, int32_t num_q_heads,
+                            int32_t num_seqs, const int32_t* cu_seqlens_q, const int32_t* seq_lens_k,
+                            int32_t max_q_len, int32_t max_kv_len, const pga_paged_kv* kv, float softmax_scale,
+                            int32_t kv_split_tokens, void* workspace, size_t workspace_bytes, void* out, float* lse,
+                            void* stream) {
+  VerifyPlan p;
+  pga::CausalArgs a;
+  pga::MergeArgs m;
+  bool nothing;
+  if (int e = prepare_verify(PGA_VERIFY_ARGS, p, a, m, nothing)) return e;
+  if (nothing || p.max_segs <= 1) return PGA_OK;
+  return launch_status(pga::launch_merge(m, max_q_len, static_cast<hipStream_t>(stream)));
+}
+
+int paged_attn_verify(const void* q, int32_t q_dtype, const float* q_descale, int32_t num_q_heads, int32_t num_seqs,
+                      const int32_t* cu_seqlens_q, const int32_t* seq_lens_k, int32_t max_q_len, int32_t max_kv_len,
+                      const pga_paged_kv* kv, float softmax_scale, int32_t kv_split_tokens, void* workspace,
+                      size_t workspace_bytes, void* out, float* lse, void* stream) {
+  VerifyPlan p;
+  pga::CausalArgs a;
+  pga::MergeArgs m;
+  bool nothing;
+  if (int e = prepare_verify(PGA_VERIFY_ARGS, p, a, m, nothing)) return e;
+  if (nothing) return PGA_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
   if (int e = launch_status(pga::launch_causal(a, false, kBF16, kv->dtype, p.max_segs, kv->num_kv_heads, num_seqs, s)))
     return e;
-  if (p.max_segs > 1) {
-    pga::MergeArgs m{};
-    m.hq = num_q_heads;
-    m.r = r;
-    m.hkv = kv->num_kv_heads;
-    m.num_seqs = num_seqs;
-    m.max_kv_len = max_kv_len;
-    m.cu_q = cu_seqlens_q;
-    m.lens_k = seq_lens_k;
-    m.seg_len = p.split;
-    m.max_segs = p.max_segs;
-    m.rows_cap = p.rows_cap;
-    m.ws_o = a.ws_o;
-    m.ws_lse = a.ws_lse;
-    m.out = a.out;
-    m.lse = lse;
-    return launch_status(pga::launch_merge(m, max_q_len, s));
-  }
+  if (p.max_segs > 1) return launch_status(pga::launch_merge(m, max_q_len, s));
   return PGA_OK;
 }
 

@@ -81,12 +81,13 @@ def to_device(p, device="cuda", kv_split_tokens: Optional[int] = None) -> Device
                          out, lse, ws)
 
 
-def run(dp: DeviceProblem, stream=None) -> torch.Tensor:
-    """One call of the entry point matching ``dp.mode``; writes dp.out / dp.lse."""
+def run(dp: DeviceProblem, stream=None, stage: str = "all") -> torch.Tensor:
+    """One call of the entry point matching ``dp.mode``; writes dp.out / dp.lse.
+    For verify, ``stage`` may select only the attention kernel or only the merge."""
     if dp.mode == "verify":
         return paged_attn_verify(dp.q, dp.cu_seqlens_q, dp.seq_lens_k, dp.max_q_len, dp.max_kv_len, dp.kv,
                                  dp.softmax_scale, dp.kv_split_tokens, q_descale=dp.q_descale, workspace=dp.workspace,
-                                 out=dp.out, lse=dp.lse, stream=stream)
+                                 out=dp.out, lse=dp.lse, stream=stream, stage=stage)
     if dp.mode == "prefill":
         return paged_attn_prefill_prefix(dp.q, dp.cu_seqlens_q, dp.cu_seqlens_k, dp.max_q_len, dp.max_kv_len, dp.kv,
                                          dp.softmax_scale, q_descale=dp.q_descale, out=dp.out, lse=dp.lse,
