@@ -106,9 +106,13 @@ typedef struct pga_paged_kv {
  * queries, 16 query heads per KV head, head size 256, page size 16, FP8 KV).
  * All r * Lq_b query rows of one KV group are packed into one tile, so each KV
  * page is loaded once for every speculative token of the group
- * (Modifications: BLOCK_M = 16 x BLOCK_Q).  Long histories are cut into
- * segments of kv_split_tokens keys whose fp32 partial results are merged by a
- * separate log-sum-exp kernel (Modifications: 8-64 segments).
+ * (Modifications: BLOCK_M = 16 x BLOCK_Q).  Long histories are split KV-wise
+ * and the fp32 partial results are merged by a separate log-sum-exp kernel
+ * (Modifications: 8-64 segments).  The split here is balanced rather than
+ * fixed: a fixed set of persistent workgroups takes equal shares of the list
+ * of (sequence, kv head, 64-key tile) work, so a history is cut where those
+ * shares end, and additionally into segments of at most kv_split_tokens keys
+ * when that is set.
  *
  *   q             [T, num_q_heads, 256] bf16 (q_dtype must be PGA_DTYPE_BF16)
  *   q_descale     device scalar or NULL; used as a factor on the scores
@@ -116,10 +120,13 @@ typedef struct pga_paged_kv {
  *   seq_lens_k    [num_seqs] int32, Lk_b >= Lq_b, including the new tokens
  *   max_q_len     host upper bound of Lq_b, 1..4; (Hq / Hkv) * max_q_len <= 64
  *   max_kv_len    host upper bound of Lk_b
- *   kv_split_tokens  0 = library's choice; otherwise the segment length, a
- *                 positive multiple of 64
+ *   kv_split_tokens  0 = no segment cap (cuts only where the balanced
+ *                 shares end); otherwise the longest piece of one history
+ *                 that one workgroup attends, a positive multiple of 64
  *   workspace     device buffer of at least paged_attn_verify_workspace_bytes()
- *                 (may be NULL when that size is 0)
+ *                 bytes, 256-byte aligned; holds fp32 partial rows and their
+ *                 lse values between the two stages; caller-owned, its
+ *                 contents on entry do not matter
  *   out           [T, num_q_heads, 256] bf16;  lse  [T, num_q_heads] fp32 or NULL
  * Returns PGA_OK or a PGA_ERR_* code.
  */
@@ -147,13 +154,16 @@ int paged_attn_verify_merge(const void* q, int32_t q_dtype, const float* q_desca
                             int32_t kv_split_tokens, void* workspace, size_t workspace_bytes, void* out,
                             float* lse, void* stream);
 
-/* Workspace bytes paged_attn_verify needs for these host bounds (0 when no
- * sequence can span more than one segment). */
+/* Workspace bytes paged_attn_verify needs for these host bounds.  A balanced
+ * split can cut any history, so this is > 0 whenever the bounds admit any
+ * work; 0 for bounds with no work (no sequences, max_kv_len 0) or invalid
+ * bounds. */
 size_t paged_attn_verify_workspace_bytes(int32_t num_q_heads, int32_t num_kv_heads, int32_t num_seqs,
                                          int32_t max_q_len, int32_t max_kv_len, int32_t kv_split_tokens);
 
-/* Segment length paged_attn_verify uses for these host bounds (after resolving
- * kv_split_tokens = 0), or 0 for invalid bounds. */
+/* Longest piece of one history that one workgroup attends for these host
+ * bounds: kv_split_tokens when set, otherwise max_kv_len rounded up to a
+ * multiple of 64 (at least 64); 0 for invalid bounds. */
 int32_t paged_attn_verify_split_tokens(int32_t num_q_heads, int32_t num_kv_heads, int32_t num_seqs,
                                        int32_t max_q_len, int32_t max_kv_len, int32_t kv_split_tokens);
 

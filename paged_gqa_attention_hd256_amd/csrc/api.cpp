@@ -20,10 +20,9 @@ constexpr int kBF16 = PGA_DTYPE_BF16;
 constexpr int kFP8 = PGA_DTYPE_FP8_E4M3;
 constexpr int kHeadDim = PGA_HEAD_DIM;
 constexpr int kMaxRowsPerGroup = 64;   // query rows of one kv group a verify workgroup holds
-constexpr int kTileKeys = 64;          // keys per LDS tile of the causal kernel
-constexpr int kTargetUnits = 1024;     // verify: workgroups to aim for (4 per CU on 256 CUs)
-constexpr int kMinSplit = 512;         // verify: shortest automatic segment
-constexpr int kMaxAutoSegments = 64;
+constexpr int kTileKeys = 64;          // keys per LDS tile of the causal kernels
+constexpr int kMinTilesPerWg = 4;      // verify: shortest run of tiles one workgroup takes
+constexpr int kMaxVerifyWgs = 1024;    // verify: cap of the persistent grid
 constexpr int kMaxGridYZ = 65535;
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
@@ -80,37 +79,47 @@ KvArgs make_kv(const pga_paged_kv* kv) {
   return a;
 }
 
-// Segment length for verify (a multiple of the 64-key tile), or 0 if invalid.
-int32_t resolve_split(int32_t num_kv_heads, int32_t num_seqs, int32_t max_kv_len, int32_t kv_split_tokens) {
-  if (kv_split_tokens < 0 || kv_split_tokens % kTileKeys != 0) return 0;
-  if (kv_split_tokens > 0) return kv_split_tokens;
-  const int64_t units = std::max<int64_t>(1, int64_t(num_seqs) * num_kv_heads);
-  const int64_t nseg = std::min<int64_t>(kMaxAutoSegments, std::max<int64_t>(1, cdiv(kTargetUnits, units)));
-  int64_t split = cdiv(std::max<int32_t>(max_kv_len, 1), nseg);
-  split = cdiv(split, kTileKeys) * kTileKeys;
-  split = std::max<int64_t>(split, kMinSplit);
-  return static_cast<int32_t>(std::min<int64_t>(split, INT32_MAX / 2));
-}
-
 struct VerifyPlan {
-  int32_t split = 0, max_segs = 1, rows_cap = 0;
+  int32_t seg_tiles = 0;   // 64-key tiles per segment
+  int32_t max_segs = 0;    // segments per (sequence, kv head), host bound
+  int32_t rows_cap = 0;    // r * max_q_len
+  int32_t wg_cap = 0;      // bound of the persistent grid (device independent)
   size_t ws_o_bytes = 0, ws_bytes = 0;
 };
 
+// Verify work plan from the host bounds.  The workspace holds one slot per
+// (segment, workgroup) piece: at most #segments + #workgroups of them.
 bool plan_verify(int32_t hq, int32_t hkv, int32_t num_seqs, int32_t max_q_len, int32_t max_kv_len,
                  int32_t kv_split_tokens, VerifyPlan& p) {
   if (hq <= 0 || hkv <= 0 || hq % hkv != 0 || num_seqs < 0 || max_q_len < 1 || max_kv_len < 0) return false;
-  p.split = resolve_split(hkv, num_seqs, max_kv_len, kv_split_tokens);
-  if (p.split <= 0) return false;
-  p.max_segs = static_cast<int32_t>(std::max<int64_t>(1, cdiv(max_kv_len, p.split)));
+  if (kv_split_tokens < 0 || kv_split_tokens % kTileKeys != 0) return false;
+  const int64_t tiles_bound = cdiv(max_kv_len, kTileKeys);
+  p.seg_tiles = kv_split_tokens > 0 ? kv_split_tokens / kTileKeys
+                                    : static_cast<int32_t>(std::max<int64_t>(1, tiles_bound));
+  p.max_segs = static_cast<int32_t>(std::max<int64_t>(1, cdiv(tiles_bound, p.seg_tiles)));
   p.rows_cap = (hq / hkv) * max_q_len;
-  if (p.max_segs > 1) {
-    const size_t units = size_t(num_seqs) * hkv * p.max_segs;
-    p.ws_o_bytes = units * p.rows_cap * kHeadDim * sizeof(float);
+  const int64_t units = int64_t(num_seqs) * hkv;
+  p.wg_cap = static_cast<int32_t>(std::min<int64_t>(kMaxVerifyWgs, std::max<int64_t>(1, cdiv(units * tiles_bound, kMinTilesPerWg))));
+  if (units > 0 && tiles_bound > 0) {
+    const size_t slots = size_t(units) * p.max_segs + p.wg_cap;
+    p.ws_o_bytes = slots * p.rows_cap * kHeadDim * sizeof(float);
     p.ws_o_bytes = (p.ws_o_bytes + 255) & ~size_t(255);
-    p.ws_bytes = p.ws_o_bytes + units * p.rows_cap * sizeof(float);
+    p.ws_bytes = p.ws_o_bytes + slots * p.rows_cap * sizeof(float);
   }
   return true;
+}
+
+// Compute units of the current device (cached per device; 256 if unknown).
+int device_cus() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] <= 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
 }
 
 int launch_status(hipError_t e) { return e == hipSuccess ? PGA_OK : PGA_ERR_LAUNCH; }
@@ -145,7 +154,7 @@ int32_t paged_attn_verify_split_tokens(int32_t num_q_heads, int32_t num_kv_heads
                                        int32_t max_q_len, int32_t max_kv_len, int32_t kv_split_tokens) {
   VerifyPlan p;
   if (!plan_verify(num_q_heads, num_kv_heads, num_seqs, max_q_len, max_kv_len, kv_split_tokens, p)) return 0;
-  return p.split;
+  return p.seg_tiles * kTileKeys;
 }
 
 // Validates a verify call and fills the launch arguments; returns a status.
@@ -153,7 +162,7 @@ static int prepare_verify(const void* q, int32_t q_dtype, const float* q_descale
                           int32_t num_seqs, const int32_t* cu_seqlens_q, const int32_t* seq_lens_k, int32_t max_q_len,
                           int32_t max_kv_len, const pga_paged_kv* kv, float softmax_scale, int32_t kv_split_tokens,
                           void* workspace, size_t workspace_bytes, void* out, float* lse, VerifyPlan& p,
-                          pga::CausalArgs& a, pga::MergeArgs& m, bool& nothing) {
+                          pga::VerifyArgs& a, int& num_wg, bool& nothing) {
   nothing = false;
   if (!q || !cu_seqlens_q || !seq_lens_k || !out || !kv) return PGA_ERR_NULL;
   if (num_seqs < 0 || num_q_heads <= 0 || max_kv_len < 0) return PGA_ERR_SHAPE;
@@ -164,52 +173,36 @@ static int prepare_verify(const void* q, int32_t q_dtype, const float* q_descale
   const int32_t r = num_q_heads / kv->num_kv_heads;
   if (int64_t(r) * max_q_len > kMaxRowsPerGroup) return PGA_ERR_UNSUPPORTED;
   if (kv_split_tokens < 0 || kv_split_tokens % kTileKeys != 0) return PGA_ERR_SHAPE;
-  if (num_seqs > kMaxGridYZ) return PGA_ERR_UNSUPPORTED;
   if (!aligned(q, 16) || !aligned(out, 8) || (lse && !aligned(lse, 4))) return PGA_ERR_UNSUPPORTED;
   if (!plan_verify(num_q_heads, kv->num_kv_heads, num_seqs, max_q_len, max_kv_len, kv_split_tokens, p))
     return PGA_ERR_SHAPE;
+  if (int64_t(num_seqs) * kv->num_kv_heads > INT32_MAX / 2) return PGA_ERR_UNSUPPORTED;
   if (p.ws_bytes > 0 && (!workspace || workspace_bytes < p.ws_bytes)) return PGA_ERR_WORKSPACE;
   if (p.ws_bytes > 0 && !aligned(workspace, 256)) return PGA_ERR_UNSUPPORTED;
   if (num_seqs == 0 || max_kv_len == 0) {
     nothing = true;
     return PGA_OK;
   }
-  a = pga::CausalArgs{};
-  a.q = q;
+  a = pga::VerifyArgs{};
+  a.q = static_cast<const uint16_t*>(q);
   a.q_ds = q_descale;
   a.hq = num_q_heads;
   a.r = r;
   a.num_seqs = num_seqs;
   a.cu_q = cu_seqlens_q;
   a.lens_k = seq_lens_k;
-  a.cu_k = nullptr;
   a.kv = make_kv(kv);
   a.c2_base = softmax_scale * 1.4426950408889634f;
   a.max_q_len = max_q_len;
   a.max_kv_len = max_kv_len;
-  a.tile_tokens = max_q_len;
-  a.seg_len = p.split;
-  a.max_segs = p.max_segs;
+  a.seg_tiles = p.seg_tiles;
   a.rows_cap = p.rows_cap;
   a.out = static_cast<uint16_t*>(out);
   a.lse = lse;
-  a.ws_o = p.ws_bytes ? static_cast<float*>(workspace) : nullptr;
-  a.ws_lse = p.ws_bytes ? reinterpret_cast<float*>(static_cast<char*>(workspace) + p.ws_o_bytes) : nullptr;
-  m = pga::MergeArgs{};
-  m.hq = num_q_heads;
-  m.r = r;
-  m.hkv = kv->num_kv_heads;
-  m.num_seqs = num_seqs;
-  m.max_kv_len = max_kv_len;
-  m.cu_q = cu_seqlens_q;
-  m.lens_k = seq_lens_k;
-  m.seg_len = p.split;
-  m.max_segs = p.max_segs;
-  m.rows_cap = p.rows_cap;
-  m.ws_o = a.ws_o;
-  m.ws_lse = a.ws_lse;
-  m.out = a.out;
-  m.lse = lse;
+  a.ws_o = static_cast<float*>(workspace);
+  a.ws_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + p.ws_o_bytes);
+  const int occupancy = kv->dtype == kFP8 ? 2 : 1;  // workgroups per CU the LDS allows
+  num_wg = std::max(1, std::min(p.wg_cap, device_cus() * occupancy));
   return PGA_OK;
 }
 
@@ -223,13 +216,12 @@ int paged_attn_verify_partials(const void* q, int32_t q_dtype, const float* q_de
                                int32_t kv_split_tokens, void* workspace, size_t workspace_bytes, void* out,
                                float* lse, void* stream) {
   VerifyPlan p;
-  pga::CausalArgs a;
-  pga::MergeArgs m;
+  pga::VerifyArgs a;
+  int num_wg = 0;
   bool nothing;
-  if (int e = prepare_verify(PGA_VERIFY_ARGS, p, a, m, nothing)) return e;
+  if (int e = prepare_verify(PGA_VERIFY_ARGS, p, a, num_wg, nothing)) return e;
   if (nothing) return PGA_OK;
-  return launch_status(pga::launch_causal(a, false, kBF16, kv->dtype, p.max_segs, kv->num_kv_heads, num_seqs,
-                                          static_cast<hipStream_t>(stream)));
+  return launch_status(pga::launch_verify(a, kv->dtype, num_wg, static_cast<hipStream_t>(stream)));
 }
 
 int paged_attn_verify_merge(const void* q, int32_t q_dtype, const float* q_descale, int32_t num_q_heads,
@@ -238,12 +230,12 @@ int paged_attn_verify_merge(const void* q, int32_t q_dtype, const float* q_desca
                             int32_t kv_split_tokens, void* workspace, size_t workspace_bytes, void* out, float* lse,
                             void* stream) {
   VerifyPlan p;
-  pga::CausalArgs a;
-  pga::MergeArgs m;
+  pga::VerifyArgs a;
+  int num_wg = 0;
   bool nothing;
-  if (int e = prepare_verify(PGA_VERIFY_ARGS, p, a, m, nothing)) return e;
-  if (nothing || p.max_segs <= 1) return PGA_OK;
-  return launch_status(pga::launch_merge(m, max_q_len, static_cast<hipStream_t>(stream)));
+  if (int e = prepare_verify(PGA_VERIFY_ARGS, p, a, num_wg, nothing)) return e;
+  if (nothing) return PGA_OK;
+  return launch_status(pga::launch_verify_merge(a, num_wg, static_cast<hipStream_t>(stream)));
 }
 
 int paged_attn_verify(const void* q, int32_t q_dtype, const float* q_descale, int32_t num_q_heads, int32_t num_seqs,
@@ -251,16 +243,14 @@ int paged_attn_verify(const void* q, int32_t q_dtype, const float* q_descale, in
                       const pga_paged_kv* kv, float softmax_scale, int32_t kv_split_tokens, void* workspace,
                       size_t workspace_bytes, void* out, float* lse, void* stream) {
   VerifyPlan p;
-  pga::CausalArgs a;
-  pga::MergeArgs m;
+  pga::VerifyArgs a;
+  int num_wg = 0;
   bool nothing;
-  if (int e = prepare_verify(PGA_VERIFY_ARGS, p, a, m, nothing)) return e;
+  if (int e = prepare_verify(PGA_VERIFY_ARGS, p, a, num_wg, nothing)) return e;
   if (nothing) return PGA_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (int e = launch_status(pga::launch_causal(a, false, kBF16, kv->dtype, p.max_segs, kv->num_kv_heads, num_seqs, s)))
-    return e;
-  if (p.max_segs > 1) return launch_status(pga::launch_merge(m, max_q_len, s));
-  return PGA_OK;
+  if (int e = launch_status(pga::launch_verify(a, kv->dtype, num_wg, s))) return e;
+  return launch_status(pga::launch_verify_merge(a, num_wg, s));
 }
 
 int paged_attn_prefill_prefix(const void* q, int32_t q_dtype, const float* q_descale, int32_t num_q_heads,
@@ -282,29 +272,23 @@ int paged_attn_prefill_prefix(const void* q, int32_t q_dtype, const float* q_des
   const int32_t tile_tokens = kMaxRowsPerGroup / r;
   const int64_t q_tiles = cdiv(max_seqlen_q, tile_tokens);
   if (q_tiles > INT32_MAX) return PGA_ERR_UNSUPPORTED;
-  pga::CausalArgs a{};
+  pga::PrefillArgs a{};
   a.q = q;
   a.q_ds = q_descale;
   a.hq = num_q_heads;
   a.r = r;
   a.num_seqs = num_seqs;
   a.cu_q = cu_seqlens_q;
-  a.lens_k = nullptr;
   a.cu_k = cu_seqlens_k;
   a.kv = make_kv(kv);
   a.c2_base = softmax_scale * 1.4426950408889634f;
   a.max_q_len = max_seqlen_q;
   a.max_kv_len = max_seqlen_k;
   a.tile_tokens = tile_tokens;
-  a.seg_len = 0;
-  a.max_segs = 1;
-  a.rows_cap = 0;
   a.out = static_cast<uint16_t*>(out);
   a.lse = lse;
-  a.ws_o = nullptr;
-  a.ws_lse = nullptr;
-  return launch_status(pga::launch_causal(a, true, q_dtype, kv->dtype, static_cast<int>(q_tiles), kv->num_kv_heads,
-                                          num_seqs, static_cast<hipStream_t>(stream)));
+  return launch_status(pga::launch_prefill(a, q_dtype, kv->dtype, static_cast<int>(q_tiles),
+                                           static_cast<hipStream_t>(stream)));
 }
 
 int sparse_paged_attn(const void* q, int32_t q_dtype, const float* q_descale, int32_t num_q_heads,

@@ -1,22 +1,26 @@
 // Wave-level attention core for 16 query rows against a 32- or 64-key tile in LDS.
 //
-// The scores are formed transposed, S^T = K * Q^T, on 16x16x32 bf16 MFMAs with
-// the keys as the M dimension and the wave's 16 query rows as N.  A lane then
-// owns one query row (n = lane % 16) and 16 of the tile's keys
+// The scores are formed transposed, S^T = K * Q^T, with the keys as the MFMA M
+// dimension and the wave's 16 query rows as N.  A lane then owns one query row
+// (n = lane % 16) and 4 * NMB of the tile's keys
 // (key = 16 * mb + 4 * (lane / 16) + i), so the row maximum and sum need only
 // in-lane work plus one reduction over the four 16-lane groups, and the
 // probabilities already sit in the B-operand layout of the P * V product:
 // O^T = V^T * P^T, with V^T read from LDS by transpose loads.
 //
 // Arithmetic (fixed by the 2e-3 rel-L2 bar; see the rounding emulator test):
-//   QK^T  bf16 x bf16 -> fp32 (FP8 keys are widened to bf16 exactly)
-//   softmax in fp32, base 2, scale folded into one multiplier
+//   QK^T  BF16 keys: bf16 x bf16 MFMA, fp32 accumulate.
+//         FP8 keys: scaled FP8 MFMA, keys used as stored; a bf16 query row is
+//         split exactly into two FP8 parts (hi + lo / 16, row scaled by a power
+//         of two) -- the same products as bf16 arithmetic without widening the
+//         keys; an FP8 query row is used as it is.
+//   softmax in fp32, base 2, scale folded into one multiplier per row.
 //   PV    FP8 V: fp16 P x fp16 V (exact widening);  BF16 V: P split into a
 //         bf16 high and low part, two bf16 MFMAs.
 //
-// LDS tile layout: row = key, row bytes RB = 256 * elt, stored in
-// 16-byte chunks whose position is XOR-swizzled by the key: logical chunk c of
-// key k sits at chunk c ^ (k & (RB / 16 - 1)).
+// LDS tile layout: row = key, row bytes RB = 256 * elt, stored in 16-byte
+// chunks whose position is XOR-swizzled by the key: logical chunk c of key k
+// sits at chunk c ^ (k & (RB / 16 - 1)).
 #pragma once
 
 #include "pga_device.h"
@@ -37,7 +41,7 @@ struct TileGeom {
 // Running state of one wave: 16 rows, full head dimension.
 struct WaveState {
   f32x4 o[16];  // O^T: o[mb][i] = O[row = lane % 16][d = 16 * mb + 4 * (lane / 16) + i]
-  float m;      // running max of the scaled scores (log2 domain), per row
+  float m;      // reference maximum of the scaled scores (log2 domain), per row
   float l;      // this lane's partial sum of probabilities (reduced over groups at the end)
   __device__ __forceinline__ void init() {
 #pragma unroll
@@ -47,42 +51,114 @@ struct WaveState {
   }
 };
 
-// Q^T operand of the 16 rows: qf[ks] holds Q[row][32 * ks + 8 * (lane / 16) + j].
-struct QFrag {
+// Q^T operand of the wave's 16 rows, by key encoding.
+//   BF16 keys: q[ks] holds Q[row][32 * ks + 8 * (lane / 16) + j] (bf16 MFMA B operand).
+//   FP8 keys:  hi[h] / lo[h] hold 32 FP8 codes of Q[row][128 * h + 32 * (lane / 16) + j]
+//     (B operand of the scaled 16x16x128 FP8 MFMA).
+// rscale multiplies the scores computed from the fragment (1 unless the row
+// was scaled before its FP8 split).
+template <int KV>
+struct QFragT;
+template <>
+struct QFragT<kBF16> {
   bf16x8 q[8];
+  float rscale;
+};
+template <>
+struct QFragT<kFP8> {
+  i32x8 hi[2];
+  i32x8 lo[2];
+  bool has_lo;
+  float rscale;
 };
 
-// Scores of a tile of 16 * NMB keys: s[mb][i] for key 16 * mb + 4 * (lane / 16) + i.
-template <int KV, int NMB>
-__device__ __forceinline__ void tile_scores(const lds_t* kt, const QFrag& qf, f32x4 (&s)[NMB]) {
+// E8M0 scale codes of the scaled FP8 MFMA: 2^0 and 2^-4.
+constexpr int kScaleOne = 127;
+constexpr int kScaleLo = 123;
+
+__device__ __forceinline__ f32x4 mfma_fp8_scaled(i32x8 a, i32x8 b, f32x4 c, int scale_b) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, kScaleOne, 0, scale_b);
+}
+
+// Split 8 query values (already multiplied by the row scale) into FP8 codes,
+// two dwords each: x = hi + lo / 16 exactly whenever |x| >= 2^-6.
+__device__ __forceinline__ void split_q8(const float (&x)[8], int& hi0, int& hi1, int& lo0, int& lo1) {
+  int h[2] = {0, 0}, l[2] = {0, 0};
+#pragma unroll
+  for (int j = 0; j < 8; j += 2) {
+    const int w = j >> 2;
+    const bool up = (j & 2) != 0;
+    const int hp = __builtin_amdgcn_cvt_pk_fp8_f32(x[j], x[j + 1], 0, false);
+    const auto back = __builtin_amdgcn_cvt_pk_f32_fp8(hp, false);
+    const int lp = __builtin_amdgcn_cvt_pk_fp8_f32((x[j] - back[0]) * 16.f, (x[j + 1] - back[1]) * 16.f, 0, false);
+    h[w] |= up ? (hp & 0xFFFF) << 16 : (hp & 0xFFFF);
+    l[w] |= up ? (lp & 0xFFFF) << 16 : (lp & 0xFFFF);
+  }
+  hi0 = h[0];
+  hi1 = h[1];
+  lo0 = l[0];
+  lo1 = l[1];
+}
+
+// Scores of a tile of 16 * NMB keys: s[mb][i] for key 16 * mb + 4 * (lane / 16) + i,
+// before the softmax scale and the fragment's rscale.  QSPLIT: the FP8 query
+// fragment has a low part (bf16 queries).
+template <int KV, int NMB, bool QSPLIT>
+__device__ __forceinline__ void tile_scores(const lds_t* kt, const QFragT<KV>& qf, f32x4 (&s)[NMB]) {
   using G = TileGeom<KV>;
   const int lane = lane_id();
   const int n = lane & 15, gq = lane >> 4;
 #pragma unroll
   for (int mb = 0; mb < NMB; ++mb) s[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if constexpr (KV == kFP8) {
+    // A operand: 32 FP8 codes of key 16 * mb + n, bytes 128 * h + 32 * gq .. + 31
+    // (logical chunks 8h + 2gq and 8h + 2gq + 1 of the key row).
+    // The low-part MFMA of a block depends on its high-part result, so all
+    // high parts of a half are issued before the low parts.
 #pragma unroll
-  for (int ks = 0; ks < 8; ++ks) {
+    for (int h = 0; h < 2; ++h) {
+      i32x8 a[NMB];
 #pragma unroll
-    for (int mb = 0; mb < NMB; ++mb) {
-      const int key = mb * 16 + n;
-      bf16x8 a;
-      if constexpr (KV == kFP8) {
-        const int byte = 32 * ks + 8 * gq;
-        a = fp8x8_to_bf16(lds_load<i32x2>(kt + G::off(key, byte >> 4) + (byte & 15)));
-      } else {
-        a = lds_load<bf16x8>(kt + G::off(key, 4 * ks + gq));
+      for (int mb = 0; mb < NMB; ++mb) {
+        const int key = mb * 16 + n;
+        const i32x4 a0 = lds_load<i32x4>(kt + G::off(key, 8 * h + 2 * gq));
+        const i32x4 a1 = lds_load<i32x4>(kt + G::off(key, 8 * h + 2 * gq + 1));
+        a[mb] = i32x8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
       }
-      s[mb] = mfma_bf16(a, qf.q[ks], s[mb]);
+#pragma unroll
+      for (int mb = 0; mb < NMB; ++mb) s[mb] = mfma_fp8_scaled(a[mb], qf.hi[h], s[mb], kScaleOne);
+      if constexpr (QSPLIT) {
+#pragma unroll
+        for (int mb = 0; mb < NMB; ++mb) s[mb] = mfma_fp8_scaled(a[mb], qf.lo[h], s[mb], kScaleLo);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+#pragma unroll
+      for (int mb = 0; mb < NMB; ++mb) {
+        const int key = mb * 16 + n;
+        const bf16x8 a = lds_load<bf16x8>(kt + G::off(key, 4 * ks + gq));
+        s[mb] = mfma_bf16(a, qf.q[ks], s[mb]);
+      }
     }
   }
 }
 
 // Online-softmax update with the tile's scores; returns the probabilities in
-// s (in place) and rescales the accumulators.  `c2` is the log2-domain score
-// multiplier.  When `masked` is true, `visible(key)` (key relative to the tile
-// start) decides which of this lane's keys count.
-template <int NMB, class Vis>
-__device__ __forceinline__ void tile_softmax(WaveState& st, f32x4 (&s)[NMB], float c2, bool masked, Vis visible) {
+// s (in place).  `c2` is this row's log2-domain score multiplier.  With
+// MASKED, `visible(key)` (key relative to the tile start) decides which of this
+// lane's keys count.
+//
+// The probabilities are taken relative to a reference maximum m that is only
+// raised when some row's tile maximum exceeds it by more than kRescaleLog2, so
+// the accumulators are rescaled a handful of times per row instead of once per
+// tile; p stays below 2^kRescaleLog2, well inside fp16 and bf16 range, and the
+// row sum l is kept relative to the same reference.
+constexpr float kRescaleLog2 = 8.0f;
+
+template <bool MASKED, int NMB, class Vis>
+__device__ __forceinline__ void tile_softmax(WaveState& st, f32x4 (&s)[NMB], float c2, Vis visible) {
   const int gq = lane_id() >> 4;
   float mt = kNegInf;
 #pragma unroll
@@ -90,15 +166,21 @@ __device__ __forceinline__ void tile_softmax(WaveState& st, f32x4 (&s)[NMB], flo
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       float x = s[mb][i] * c2;
-      if (masked && !visible(mb * 16 + 4 * gq + i)) x = kNegInf;
+      if constexpr (MASKED) x = visible(mb * 16 + 4 * gq + i) ? x : kNegInf;
       s[mb][i] = x;
       mt = fmaxf(mt, x);
     }
   }
   mt = group4_max(mt);
-  const float m_new = fmaxf(st.m, mt);
-  const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-  const float alpha = fast_exp2(st.m - m_use);
+  if (__builtin_amdgcn_ballot_w64(mt > st.m + kRescaleLog2) != 0) {  // wave-uniform
+    const float m_new = fmaxf(st.m, mt);
+    const float alpha = fast_exp2(st.m - m_new);  // 0 when st.m is -inf
+    st.l *= alpha;
+#pragma unroll
+    for (int d = 0; d < 16; ++d) st.o[d] *= alpha;
+    st.m = m_new;
+  }
+  const float m_use = (st.m == kNegInf) ? 0.f : st.m;
   float sum = 0.f;
 #pragma unroll
   for (int mb = 0; mb < NMB; ++mb) {
@@ -109,10 +191,7 @@ __device__ __forceinline__ void tile_softmax(WaveState& st, f32x4 (&s)[NMB], flo
       sum += p;
     }
   }
-  st.l = st.l * alpha + sum;
-  st.m = m_new;
-#pragma unroll
-  for (int d = 0; d < 16; ++d) st.o[d] *= alpha;
+  st.l += sum;
 }
 
 // O^T += V^T * P^T over the tile's 16 * NMB keys (32-key MFMA steps).

@@ -23,37 +23,38 @@ struct KvArgs {
   const float* v_ds;
 };
 
-// Bottom-right causal attention over a paged cache: speculative verify (one
-// workgroup per key segment, all query tokens of the sequence) or prefill (one
-// workgroup per tile of query tokens, all keys up to the tile's diagonal).
-struct CausalArgs {
-  const void* q;           // [T, hq, 256] bf16 or FP8 codes
+// Speculative verify: persistent stream-K grid over the key tiles of every
+// (sequence, kv head) unit; see verify.hip.
+struct VerifyArgs {
+  const uint16_t* q;       // [T, hq, 256] bf16
   const float* q_ds;
   int32_t hq, r, num_seqs;
   const int32_t* cu_q;
-  const int32_t* lens_k;   // verify: [B] key lengths
-  const int32_t* cu_k;     // prefill: [B + 1] key prefix sums
+  const int32_t* lens_k;
   KvArgs kv;
   float c2_base;           // softmax_scale * log2(e)
   int32_t max_q_len;       // host bounds: per-sequence lengths are clamped to them, so a
   int32_t max_kv_len;      //   caller that exceeds them cannot push an access out of bounds
-  int32_t tile_tokens;     // prefill: query tokens per workgroup
-  int32_t seg_len;         // verify: keys per segment (multiple of 64)
-  int32_t max_segs;        // verify: segment slots per (sequence, kv head) in the workspace
-  int32_t rows_cap;        // verify: r * max_q_len row slots per unit in the workspace
+  int32_t seg_tiles;       // 64-key tiles per segment (a partial never spans two segments)
+  int32_t rows_cap;        // r * max_q_len: row slots per workspace slot
   uint16_t* out;           // [T, hq, 256] bf16
   float* lse;              // [T, hq] or null
-  float* ws_o;             // [B, hkv, max_segs, rows_cap, 256] fp32, normalised and v-descaled
-  float* ws_lse;           // [B, hkv, max_segs, rows_cap] fp32 natural-log lse
+  float* ws_o;             // [slots, rows_cap, 256] fp32 partial outputs (normalised, v-descaled)
+  float* ws_lse;           // [slots, rows_cap] fp32 natural-log lse of the partials
 };
 
-struct MergeArgs {
-  int32_t hq, r, hkv, num_seqs, max_kv_len;
+// Prefill against a cached prefix: one workgroup per (tile of query tokens,
+// kv head, sequence), all keys up to the tile's last diagonal position.
+struct PrefillArgs {
+  const void* q;           // [T, hq, 256] bf16 or FP8 codes
+  const float* q_ds;
+  int32_t hq, r, num_seqs;
   const int32_t* cu_q;
-  const int32_t* lens_k;
-  int32_t seg_len, max_segs, rows_cap;
-  const float* ws_o;
-  const float* ws_lse;
+  const int32_t* cu_k;     // [B + 1] key prefix sums
+  KvArgs kv;
+  float c2_base;
+  int32_t max_q_len, max_kv_len;
+  int32_t tile_tokens;     // query tokens per workgroup
   uint16_t* out;
   float* lse;
 };
@@ -74,9 +75,9 @@ struct SparseArgs {
 };
 
 // Launchers (defined next to their kernels).  They return the launch status.
-hipError_t launch_causal(const CausalArgs& a, bool prefill, int q_dtype, int kv_dtype, int grid_x, int grid_y,
-                         int grid_z, hipStream_t s);
-hipError_t launch_merge(const MergeArgs& a, int max_q_len, hipStream_t s);
+hipError_t launch_verify(const VerifyArgs& a, int kv_dtype, int num_wg, hipStream_t s);
+hipError_t launch_verify_merge(const VerifyArgs& a, int num_wg, hipStream_t s);
+hipError_t launch_prefill(const PrefillArgs& a, int q_dtype, int kv_dtype, int q_tiles, hipStream_t s);
 hipError_t launch_sparse(const SparseArgs& a, int kv_dtype, hipStream_t s);
 
 }  // namespace pga

@@ -65,9 +65,21 @@ __device__ __forceinline__ void barrier() {
 }
 
 // 16-byte global -> LDS copy; `lds_wave_base` must be the same for the whole
-// wave (lane l writes lds_wave_base + 16 * l).
+// wave (lane l writes lds_wave_base + 16 * l).  Issued from inline assembly so
+// the compiler does not treat every later LDS read as possibly aliasing the
+// copy in flight (it would wait for all of them); the kernels wait on this
+// wave's copies explicitly with wait_vmcnt.  Compiler-generated waits for its
+// own loads stay correct, only more conservative, because the counter retires
+// loads in issue order.
 __device__ __forceinline__ void dma16(const void* src, lds_t* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds(src, (void __attribute__((address_space(3)))*)lds_wave_base, 16, 0, 0);
+  const unsigned base = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)lds_wave_base);
+  asm volatile(
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, off"
+      :
+      : "v"(src), "s"(base)
+      : "memory", "m0");
 }
 
 template <class T>

@@ -1,0 +1,62 @@
+// Prefill of new tokens against a cached prefix, bottom-right causal.
+//
+// One workgroup per (tile of query tokens, kv head, sequence): the tile packs
+// 64 / r tokens x r heads of one kv group (token-major rows), and streams all
+// keys from 0 to the tile's last diagonal position, with the mask of ROCm/ATOM
+// PR #2534 (FMHA commit message: the cached + new keys are longer than the
+// queries and the causal mask is bottom-right aligned).  Pages are read in the
+// kernel, with no gather to contiguous memory first (ROCm/ATOM PR #2830, recipe
+// commit).  Workgroups are ordered longest first.
+#include "causal_stream.h"
+
+namespace pga {
+
+template <int QDT, int KV>
+__global__ __launch_bounds__(256, (KV == kFP8) ? 2 : 1) void prefill_kernel(PrefillArgs a) {
+  __shared__ CausalSmem<KV> sm;
+  const int g = blockIdx.y, b = blockIdx.z;
+  const int tok0 = a.cu_q[b];
+  const int lq = min(a.cu_q[b + 1] - tok0, a.max_q_len);
+  const int lk = min(a.cu_k[b + 1] - a.cu_k[b], a.max_kv_len);
+  // Longest first: block 0 takes the last query tile, which sees the most keys.
+  const int t_lo = (gridDim.x - 1 - blockIdx.x) * a.tile_tokens;
+  if (t_lo >= lq) return;
+  const int t_hi = min(t_lo + a.tile_tokens, lq);
+  const int k_hi = lk - lq + t_hi;  // one past the last visible key of the tile
+  const int rows = a.r * (t_hi - t_lo);
+
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = lane_id();
+  const int rho = 16 * w + (lane & 15);
+  const bool row_ok = rho < rows;
+  const int tq = row_ok ? rho / a.r : 0;
+  const int t = t_lo + tq;
+  const int head = g * a.r + (row_ok ? rho - tq * a.r : 0);
+  const int64_t tok = tok0 + t;
+  QFragT<KV> qf;
+  load_q<QDT, KV>(qf, a.q, tok, a.hq, head, row_ok);
+  const float c2 = a.c2_base * load_scale(a.q_ds) * load_scale(a.kv.k_ds);
+  const int klim = row_ok ? min(lk - lq + t, k_hi - 1) : -1;
+  const int min_lim = min(lk - lq + t_lo, k_hi - 1);
+  WaveState st;
+  st.init();
+  const bool active = 16 * w < rows;
+  stream_keys<QDT, KV>(sm, a.kv, a.kv.bt + (int64_t)b * a.kv.bt_stride, g, 0, k_hi, qf, c2 * qf.rscale, klim,
+                       min_lim, active, st);
+  if (!active) return;
+  const float lrow = group4_sum(st.l);
+  if (row_ok) store_out(st, lrow, load_scale(a.kv.v_ds), a.out, a.lse, tok, a.hq, head);
+}
+
+hipError_t launch_prefill(const PrefillArgs& a, int q_dtype, int kv_dtype, int q_tiles, hipStream_t s) {
+  dim3 grid(q_tiles, a.kv.num_kv_heads, a.num_seqs), block(256);
+  if (q_dtype == kFP8 && kv_dtype == kFP8)
+    hipLaunchKernelGGL((prefill_kernel<kFP8, kFP8>), grid, block, 0, s, a);
+  else if (q_dtype == kBF16 && kv_dtype == kFP8)
+    hipLaunchKernelGGL((prefill_kernel<kBF16, kFP8>), grid, block, 0, s, a);
+  else
+    hipLaunchKernelGGL((prefill_kernel<kBF16, kBF16>), grid, block, 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace pga

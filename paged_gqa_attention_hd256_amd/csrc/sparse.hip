@@ -15,8 +15,7 @@
 // comes from the table, and runs the shared attention core on each tile.
 // Because the table is read from LDS, no vector-memory load sits between the
 // DMA instructions and their counter can be waited on exactly.
-#include "attn_core.h"
-#include "pga_args.h"
+#include "causal_stream.h"
 
 namespace pga {
 
@@ -69,16 +68,9 @@ __global__ __launch_bounds__(SparseCfg<KV>::kWaves * 64) void sparse_kernel(Spar
   const int hh = 16 * rb + n;
   const bool row_ok = hh < a.r;
   const int head = g * a.r + hh;
-  QFrag qf;
-  if (row_ok) {
-    const bf16x8* qp = reinterpret_cast<const bf16x8*>(a.q + ((int64_t)tok * a.hq + head) * kHeadDim);
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) qf.q[ks] = qp[4 * ks + gq];
-  } else {
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) qf.q[ks] = bf16x8{};
-  }
-  const float c2 = a.c2_base * load_scale(a.q_ds) * load_scale(a.kv.k_ds);
+  QFragT<KV> qf;
+  load_q<kBF16, KV>(qf, a.q, tok, a.hq, head, row_ok);
+  const float c2 = a.c2_base * load_scale(a.q_ds) * load_scale(a.kv.k_ds) * qf.rscale;
   const uint8_t* kbase = a.kv.k + g * a.kv.k_sh;
   const uint8_t* vbase = a.kv.v + g * a.kv.v_sh;
   const int32_t* bt_row = a.kv.bt + (int64_t)b * a.kv.bt_stride;
@@ -133,11 +125,11 @@ __global__ __launch_bounds__(SparseCfg<KV>::kWaves * 64) void sparse_kernel(Spar
       const lds_t* kt = tiles + (2 * (it & 1) + 0) * C::kTileBytes;
       const lds_t* vt = tiles + (2 * (it & 1) + 1) * C::kTileBytes;
       f32x4 sc[2];
-      tile_scores<KV, 2>(kt, qf, sc);
+      tile_scores<KV, 2, true>(kt, qf, sc);
       const lds_t* tt = table + 4 * (it * C::kTileKeys);
       const i32x4 v0 = lds_load<i32x4>(tt + 4 * (4 * gq));
       const i32x4 v1 = lds_load<i32x4>(tt + 4 * (16 + 4 * gq));
-      tile_softmax<2>(st, sc, c2, true, [&](int key) {
+      tile_softmax<true>(st, sc, c2, [&](int key) {
         const int q = key - 4 * gq;  // 0..3 in block 0, 16..19 in block 1
         const int e = q & 3;
         const int v = (q < 16) ? v0[e] : v1[e];

@@ -1,235 +1,257 @@
-// Bottom-right causal attention over the paged cache (speculative verify and
-// prefix prefill) and the split-KV log-sum-exp merge.
+// Speculative-verify attention with balanced split-KV and a separate
+// log-sum-exp merge kernel.
 //
-// Verify: one workgroup per (key segment, kv head, sequence).  All r * Lq_b
-// query rows of the kv group (token-major: row = t * r + h) are packed into
-// the workgroup, 16 rows per wave, so every KV page of the segment is fetched
-// from HBM once for all speculative tokens -- the reuse SGLang PR #36330 adds
-// (Motivation; Modifications: BLOCK_M = 16 x BLOCK_Q).  A sequence whose keys
-// fit one segment writes bf16 output directly; longer ones write fp32 partial
-// outputs (already divided by their row sums) and natural-log lse values that
-// lse_merge_kernel combines (Modifications: segments chosen from CU
-// parallelism and per-segment KV work).
+// All r * Lq_b query rows of a kv group (token-major: row = t * r + h) sit in
+// one workgroup, 16 rows per wave, so every KV page is fetched from HBM once
+// for all speculative tokens of the group -- the reuse SGLang PR #36330 adds
+// (Motivation; Modifications: BLOCK_M = 16 x BLOCK_Q).
 //
-// Prefill: one workgroup per (tile of query tokens, kv head, sequence), all
-// keys from 0 to the tile's last diagonal position, with the bottom-right rule
-// of ROCm/ATOM PR #2534 (FMHA commit message: keys longer than queries).
-// Pages are read in the kernel, no gather first (ROCm/ATOM PR #2830, recipe
-// commit).
-//
-// Keys stream through LDS in 64-key tiles by 16-byte global->LDS DMA,
-// double-buffered; block-table entries are read with scalar loads, so the only
-// vector-memory traffic in the loop is the DMA and its counter can be waited
-// on exactly.
-#include "attn_core.h"
-#include "pga_args.h"
+// Work split.  The 64-key tiles of every (sequence, kv head) unit, each unit
+// optionally cut into segments of at most kv_split_tokens keys, are laid end to
+// end; a persistent grid of P workgroups takes equal contiguous runs of that
+// list (stream-K).  A run that covers a whole single-segment unit writes the
+// bf16 output directly; any other piece (segment sigma, workgroup w) writes its
+// fp32 partial output, already divided by its row sums, and natural-log lse to
+// workspace slot sigma + w.  Pieces are ordered in both sigma and w, so that
+// slot is unique, and there are at most (#segments + P) of them.  The merge
+// kernel recomputes the same plan and combines each row's pieces with weights
+// exp(lse - max lse).  This replaces a fixed segment count, which on a batch
+// of uneven lengths leaves a nearly empty second round of workgroups
+// (Modifications: segments chosen from CU parallelism and per-segment work).
+#include "causal_stream.h"
 
 namespace pga {
 
-template <bool PREFILL, int QDT, int KV>
-__global__ __launch_bounds__(256, (KV == kFP8) ? 2 : 1) void causal_kernel(CausalArgs a) {
-  using G = TileGeom<KV>;
-  constexpr int kRowsPerDma = 1024 / G::kRowBytes;  // rows one 1 KB DMA instruction fills
-  constexpr int kDmaPerWave = 16 / kRowsPerDma;     // instructions per wave for its 16 rows of K (or V)
-  __shared__ __attribute__((aligned(16))) char smem[2][2][G::template tile_bytes<64>()];  // [buffer][K, V]
+constexpr int kMinTilesPerWg = 4;  // shortest run a workgroup takes (256 keys)
 
-  const int g = blockIdx.y, b = blockIdx.z;
-  const int tok0 = a.cu_q[b];
-  const int lq = min(a.cu_q[b + 1] - tok0, a.max_q_len);
-  const int lk = min(PREFILL ? a.cu_k[b + 1] - a.cu_k[b] : a.lens_k[b], a.max_kv_len);
-  // Query tokens [t_lo, t_hi) of the sequence and keys [k_lo, k_hi) this workgroup covers.
-  int t_lo, t_hi, k_lo, k_hi, seg = 0, nseg_b = 1;
-  if constexpr (PREFILL) {
-    // Longest-first: block 0 takes the last query tile, which sees the most keys.
-    t_lo = (gridDim.x - 1 - blockIdx.x) * a.tile_tokens;
-    t_hi = min(t_lo + a.tile_tokens, lq);
-    if (t_lo >= lq) return;
-    k_lo = 0;
-    k_hi = lk - lq + t_hi;  // one past the last token's last visible key
-  } else {
-    seg = blockIdx.x;
-    t_lo = 0;
-    t_hi = lq;
-    k_lo = seg * a.seg_len;
-    if (lq <= 0 || k_lo >= lk) return;
-    k_hi = min(k_lo + a.seg_len, lk);
-    nseg_b = (lk + a.seg_len - 1) / a.seg_len;
+// Per-sequence work of the plan: 64-key tiles per kv head and segments per kv head.
+struct SeqWork {
+  int tiles, segs;
+};
+__device__ __forceinline__ SeqWork seq_work_of(const VerifyArgs& a, int lq, int lk) {
+  lq = min(lq, a.max_q_len);
+  lk = min(lk, a.max_kv_len);
+  SeqWork s;
+  s.tiles = (lq > 0 && lk > 0) ? (lk + 63) >> 6 : 0;
+  s.segs = s.tiles > 0 ? (s.tiles + a.seg_tiles - 1) / a.seg_tiles : 0;
+  return s;
+}
+// Uniform b: scalar loads.
+__device__ __forceinline__ SeqWork seq_work(const VerifyArgs& a, int b) {
+  return seq_work_of(a, scalar_load(a.cu_q + b + 1) - scalar_load(a.cu_q + b), scalar_load(a.lens_k + b));
+}
+// Per-lane b (out of range gives no work).
+__device__ __forceinline__ SeqWork seq_work_lane(const VerifyArgs& a, int b) {
+  if (b >= a.num_seqs) return SeqWork{0, 0};
+  return seq_work_of(a, a.cu_q[b + 1] - a.cu_q[b], a.lens_k[b]);
+}
+
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off);
+    if (lane >= off) x += y;
   }
-  const int rows = a.r * (t_hi - t_lo);
+  return x;
+}
 
+// Plan of one call, identical in every workgroup of both kernels: total tiles,
+// tiles per workgroup, and the tile / segment prefix (per kv head) of sequence
+// `target_b`, or of the sequence holding tile `target_t` when target_b < 0.
+// Called by a whole wave.
+struct PlanPos {
+  int total, tpw, b, tile_prefix, seg_prefix;
+};
+__device__ PlanPos plan_scan(const VerifyArgs& a, int num_wg, int target_t, int target_b) {
+  const int lane = lane_id();
+  const int hkv = a.kv.num_kv_heads;
+  int tot = 0;
+  for (int c = 0; c < a.num_seqs; c += 64) tot += __shfl(wave_incl_scan(seq_work_lane(a, c + lane).tiles), 63);
+  PlanPos p;
+  p.total = tot * hkv;
+  p.tpw = max(kMinTilesPerWg, (p.total + num_wg - 1) / num_wg);
+  p.b = -1;
+  p.tile_prefix = p.seg_prefix = 0;
+  int ts = 0, ss = 0;
+  for (int c = 0; c < a.num_seqs; c += 64) {
+    const int b = c + lane;
+    const SeqWork s = seq_work_lane(a, b);
+    const int it = wave_incl_scan(s.tiles), is = wave_incl_scan(s.segs);
+    bool hit;
+    if (target_b >= 0)
+      hit = (b == target_b);
+    else
+      hit = s.tiles > 0 && (ts + it - s.tiles) * hkv <= target_t && target_t < (ts + it) * hkv;
+    const uint64_t m = __builtin_amdgcn_ballot_w64(hit);
+    if (m) {
+      const int src = __builtin_ctzll(m);
+      p.b = c + src;
+      p.tile_prefix = ts + __shfl(it - s.tiles, src);
+      p.seg_prefix = ss + __shfl(is - s.segs, src);
+      break;
+    }
+    ts += __shfl(it, 63);
+    ss += __shfl(is, 63);
+  }
+  return p;
+}
+
+template <int KV>
+__global__ __launch_bounds__(256, (KV == kFP8) ? 2 : 1) void verify_kernel(VerifyArgs a) {
+  __shared__ CausalSmem<KV> sm;
+  __shared__ int plan_lds[5];
+  const int wg = blockIdx.x, num_wg = gridDim.x;
+  const int hkv = a.kv.num_kv_heads;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = lane_id();
   const int n = lane & 15, gq = lane >> 4;
-  const int rho = 16 * w + n;
-  const bool row_ok = rho < rows;
-  const int tq = row_ok ? rho / a.r : 0;
-  const int hh = row_ok ? rho - tq * a.r : 0;
-  const int t = t_lo + tq;
-  const int64_t tok = tok0 + t;
-  const int head = g * a.r + hh;
-  const bool wave_active = 16 * w < rows;
 
-  QFrag qf;
-#pragma unroll
-  for (int ks = 0; ks < 8; ++ks) qf.q[ks] = bf16x8{};
-  if (row_ok) {
-    if constexpr (QDT == kFP8) {
-      const i32x2* qp = reinterpret_cast<const i32x2*>(static_cast<const uint8_t*>(a.q) + (tok * a.hq + head) * kHeadDim);
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks) qf.q[ks] = fp8x8_to_bf16(qp[4 * ks + gq]);
-    } else {
-      const bf16x8* qp = reinterpret_cast<const bf16x8*>(static_cast<const uint16_t*>(a.q) + (tok * a.hq + head) * kHeadDim);
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks) qf.q[ks] = qp[4 * ks + gq];
+  if (w == 0) {
+    // This workgroup's run starts at tile wg * tpw; tpw needs the total first.
+    const PlanPos p0 = plan_scan(a, num_wg, 0, 0);
+    const int t0 = wg * p0.tpw;
+    const PlanPos p = t0 < p0.total ? plan_scan(a, num_wg, t0, -1) : p0;
+    if (lane == 0) {
+      plan_lds[0] = t0 < p0.total ? p.b : -1;
+      plan_lds[1] = p0.tpw;
+      plan_lds[2] = p0.total;
+      plan_lds[3] = p.tile_prefix;
+      plan_lds[4] = p.seg_prefix;
     }
   }
+  __syncthreads();
+  int b = __builtin_amdgcn_readfirstlane(plan_lds[0]);
+  const int tpw = __builtin_amdgcn_readfirstlane(plan_lds[1]);
+  const int total = __builtin_amdgcn_readfirstlane(plan_lds[2]);
+  const int tprefix = __builtin_amdgcn_readfirstlane(plan_lds[3]);
+  const int sprefix = __builtin_amdgcn_readfirstlane(plan_lds[4]);
+  const int t0 = wg * tpw;
+  if (b < 0 || t0 >= total) return;
+  const int t1 = min(t0 + tpw, total);
+  SeqWork sw = seq_work(a, b);
+  int g = (t0 - tprefix * hkv) / sw.tiles;
+  int tu = tprefix * hkv + g * sw.tiles;  // first tile of unit (b, g) in the flattened list
+  int su = sprefix * hkv + g * sw.segs;   // first segment of unit (b, g)
   const float c2 = a.c2_base * load_scale(a.q_ds) * load_scale(a.kv.k_ds);
-  // Largest visible key of this lane's row, and the smallest such limit over
-  // the workgroup's rows (bottom-right causal, clipped to the key range).
-  const int klim = row_ok ? min(lk - lq + t, k_hi - 1) : -1;
-  const int min_lim = min(lk - lq + t_lo, k_hi - 1);
-
-  const int ntiles = (k_hi - k_lo + 63) >> 6;
-  const uint8_t* kbase = a.kv.k + g * a.kv.k_sh;
-  const uint8_t* vbase = a.kv.v + g * a.kv.v_sh;
-  const int32_t* bt_row = a.kv.bt + (int64_t)b * a.kv.bt_stride;
-
-  // Issue the DMA of tile `it` into buffer `buf`: this wave fetches tile rows
-  // 16w .. 16w + 15, which lie in one page (pages hold >= 16 tokens and tiles
-  // start at multiples of 64).
-  auto issue = [&](int it, int buf) {
-    const int tb = k_lo + it * 64;
-    const int key0 = tb + 16 * w;
-    int page = -1;
-    if (key0 < k_hi) page = bt_row[key0 >> a.kv.page_shift];
-    page = __builtin_amdgcn_readfirstlane(page);
-    const bool page_ok = page >= 0 && page < a.kv.num_pages;
-    const int64_t kpage = (int64_t)page * a.kv.k_sp;
-    const int64_t vpage = (int64_t)page * a.kv.v_sp;
-#pragma unroll
-    for (int u = 0; u < kDmaPerWave; ++u) {
-      const int row0 = 16 * w + u * kRowsPerDma;
-      const int row = row0 + lane / G::kChunks;
-      const int chunk = (lane % G::kChunks) ^ (row & (G::kChunks - 1));
-      const int key = tb + row;
-      const bool ok = page_ok && key < k_hi;
-      const int slot = key & (a.kv.page_size - 1);
-      const uint8_t* ks = ok ? kbase + kpage + slot * a.kv.k_st + chunk * 16 : reinterpret_cast<const uint8_t*>(g_zero16);
-      const uint8_t* vs = ok ? vbase + vpage + slot * a.kv.v_st + chunk * 16 : reinterpret_cast<const uint8_t*>(g_zero16);
-      dma16(ks, (lds_t*)&smem[buf][0][row0 * G::kRowBytes]);
-      dma16(vs, (lds_t*)&smem[buf][1][row0 * G::kRowBytes]);
-    }
-  };
-
-  WaveState st;
-  st.init();
-  issue(0, 0);
-  for (int it = 0; it < ntiles; ++it) {
-    if (it + 1 < ntiles) {
-      issue(it + 1, (it + 1) & 1);
-      wait_vmcnt<2 * kDmaPerWave>();
-    } else {
-      wait_vmcnt<0>();
-    }
-    barrier();
-    if (wave_active) {
-      const lds_t* kt = (const lds_t*)&smem[it & 1][0][0];
-      const lds_t* vt = (const lds_t*)&smem[it & 1][1][0];
-      const int tb = k_lo + it * 64;
-      f32x4 sc[4];
-      tile_scores<KV, 4>(kt, qf, sc);
-      const int lim = klim - tb;
-      tile_softmax<4>(st, sc, c2, tb + 63 > min_lim, [lim](int key) { return key <= lim; });
-      tile_pv<KV, 4>(st, vt, sc);
-    }
-    barrier();
-  }
-
-  if (!wave_active) return;
-  const float lrow = group4_sum(st.l);
-  if (!row_ok) return;
   const float vds = load_scale(a.kv.v_ds);
-  const float inv = lrow > 0.f ? vds / lrow : 0.f;
-  const float lse = lrow > 0.f ? (st.m + log2f(lrow)) * kLn2 : kNegInf;
-  if (nseg_b == 1) {
-    uint16_t* op = a.out + (tok * a.hq + head) * kHeadDim + 4 * gq;
+
+  int cur = t0;
+  while (cur < t1) {
+    const int lt0 = cur - tu;
+    const int s = lt0 / a.seg_tiles;
+    const int lts1 = min((s + 1) * a.seg_tiles, sw.tiles);
+    const int lt1 = min(lts1, t1 - tu);
+    const int tok0 = scalar_load(a.cu_q + b);
+    const int lq = min(scalar_load(a.cu_q + b + 1) - tok0, a.max_q_len);
+    const int lk = min(scalar_load(a.lens_k + b), a.max_kv_len);
+    const int rows = min(a.r * lq, a.rows_cap);
+    const int rho = 16 * w + n;
+    const bool row_ok = rho < rows;
+    const int t = row_ok ? rho / a.r : 0;
+    const int head = g * a.r + (row_ok ? rho - t * a.r : 0);
+    const int64_t tok = tok0 + t;
+    const bool wave_active = 16 * w < rows;
+    QFragT<KV> qf;
+    load_q<kBF16, KV>(qf, a.q, tok, a.hq, head, row_ok);
+    const int k_lo = lt0 * 64, k_hi = min(lt1 * 64, lk);
+    const int klim = row_ok ? min(lk - lq + t, k_hi - 1) : -1;
+    const int min_lim = min(lk - lq, k_hi - 1);
+    WaveState st;
+    st.init();
+    stream_keys<kBF16, KV>(sm, a.kv, a.kv.bt + (int64_t)b * a.kv.bt_stride, g, k_lo, k_hi, qf, c2 * qf.rscale,
+                           klim, min_lim, wave_active, st);
+    if (wave_active) {
+      const float lrow = group4_sum(st.l);
+      const bool whole = lt0 == s * a.seg_tiles && lt1 == lts1;
+      if (row_ok) {
+        if (whole && sw.segs == 1) {
+          store_out(st, lrow, vds, a.out, a.lse, tok, a.hq, head);
+        } else {
+          const int64_t slot = (int64_t)su + s + wg;
+          const float inv = lrow > 0.f ? vds / lrow : 0.f;
+          float* wp = a.ws_o + (slot * a.rows_cap + rho) * kHeadDim + 4 * gq;
 #pragma unroll
-    for (int mb = 0; mb < 16; ++mb) {
-      const uint32_t lo = pack_bf16x2(st.o[mb][0] * inv, st.o[mb][1] * inv);
-      const uint32_t hi = pack_bf16x2(st.o[mb][2] * inv, st.o[mb][3] * inv);
-      *reinterpret_cast<uint2*>(op + 16 * mb) = make_uint2(lo, hi);
+          for (int mb = 0; mb < 16; ++mb) *reinterpret_cast<f32x4*>(wp + 16 * mb) = st.o[mb] * inv;
+          if (gq == 0) a.ws_lse[slot * a.rows_cap + rho] = lrow > 0.f ? (st.m + log2f(lrow)) * kLn2 : kNegInf;
+        }
+      }
     }
-    if (gq == 0 && a.lse) a.lse[tok * a.hq + head] = lse;
-  } else {
-    const int64_t unit = ((int64_t)b * a.kv.num_kv_heads + g) * a.max_segs + seg;
-    float* wp = a.ws_o + (unit * a.rows_cap + rho) * kHeadDim + 4 * gq;
-#pragma unroll
-    for (int mb = 0; mb < 16; ++mb) *reinterpret_cast<f32x4*>(wp + 16 * mb) = st.o[mb] * inv;
-    if (gq == 0) a.ws_lse[unit * a.rows_cap + rho] = lse;
+    cur = tu + lt1;
+    if (lt1 == sw.tiles) {  // next unit: next kv head, or the next sequence with work
+      tu += sw.tiles;
+      su += sw.segs;
+      if (++g == hkv) {
+        g = 0;
+        do {
+          if (++b >= a.num_seqs) break;
+          sw = seq_work(a, b);
+        } while (sw.tiles == 0);
+        if (b >= a.num_seqs) break;
+      }
+    }
   }
 }
 
-// Combine the segments of one (token, head): weights exp(lse_s - max lse),
-// segments with lse = -inf (no visible key) contribute nothing.  One wave per
-// (token, head); each lane owns four consecutive output elements.
-__global__ __launch_bounds__(256) void lse_merge_kernel(MergeArgs a) {
-  const int b = blockIdx.y;
-  const int pair = blockIdx.x * 4 + (threadIdx.x >> 6);
+// One wave per (unit, query row): the pieces of every segment of the unit, as
+// laid out by verify_kernel, combined with log-sum-exp weights.  Pieces with
+// lse = -inf (no visible key) contribute nothing.
+__global__ __launch_bounds__(256) void verify_merge_kernel(VerifyArgs a, int num_wg) {
+  const int hkv = a.kv.num_kv_heads;
+  const int u = blockIdx.x;
+  const int b = u / hkv, g = u - (u / hkv) * hkv;
+  const int rho = blockIdx.y * 4 + (threadIdx.x >> 6);
   const int lane = lane_id();
-  const int t = pair / a.hq, h = pair - (pair / a.hq) * a.hq;
+  const SeqWork sw = seq_work(a, b);
+  if (sw.tiles == 0) return;
   const int tok0 = a.cu_q[b];
-  const int lq = a.cu_q[b + 1] - tok0;
-  if (t >= lq) return;
-  const int lk = min(a.lens_k[b], a.max_kv_len);
-  const int nseg = min((lk + a.seg_len - 1) / a.seg_len, a.max_segs);
-  if (nseg <= 1) return;
-  const int g = h / a.r;
-  const int rho = t * a.r + (h - g * a.r);
-  if (rho >= a.rows_cap) return;
-  const int64_t unit0 = ((int64_t)b * a.hkv + g) * a.max_segs;
+  const int lq = min(a.cu_q[b + 1] - tok0, a.max_q_len);
+  if (rho >= min(a.r * lq, a.rows_cap)) return;
+  const PlanPos p = plan_scan(a, num_wg, 0, b);
+  const int tu = p.tile_prefix * hkv + g * sw.tiles;
+  const int su = p.seg_prefix * hkv + g * sw.segs;
+  if (sw.segs == 1 && tu / p.tpw == (tu + sw.tiles - 1) / p.tpw) return;  // written directly
   float mx = kNegInf;
-  for (int s = 0; s < nseg; ++s) mx = fmaxf(mx, a.ws_lse[(unit0 + s) * a.rows_cap + rho]);
+  for (int s = 0; s < sw.segs; ++s) {
+    const int ts0 = tu + s * a.seg_tiles, ts1 = tu + min((s + 1) * a.seg_tiles, sw.tiles);
+    for (int wk = ts0 / p.tpw; wk <= (ts1 - 1) / p.tpw; ++wk)
+      mx = fmaxf(mx, a.ws_lse[((int64_t)su + s + wk) * a.rows_cap + rho]);
+  }
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float wsum = 0.f;
   if (mx != kNegInf) {
-    for (int s = 0; s < nseg; ++s) {
-      const float ls = a.ws_lse[(unit0 + s) * a.rows_cap + rho];
-      if (ls == kNegInf) continue;
-      const float wgt = __expf(ls - mx);
-      wsum += wgt;
-      const f32x4 o = *reinterpret_cast<const f32x4*>(a.ws_o + ((unit0 + s) * a.rows_cap + rho) * kHeadDim + 4 * lane);
-      acc += wgt * o;
+    for (int s = 0; s < sw.segs; ++s) {
+      const int ts0 = tu + s * a.seg_tiles, ts1 = tu + min((s + 1) * a.seg_tiles, sw.tiles);
+      for (int wk = ts0 / p.tpw; wk <= (ts1 - 1) / p.tpw; ++wk) {
+        const int64_t slot = (int64_t)su + s + wk;
+        const float ls = a.ws_lse[slot * a.rows_cap + rho];
+        if (ls == kNegInf) continue;
+        const float wgt = __expf(ls - mx);
+        wsum += wgt;
+        acc += wgt * *reinterpret_cast<const f32x4*>(a.ws_o + (slot * a.rows_cap + rho) * kHeadDim + 4 * lane);
+      }
     }
   }
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+  const int t = rho / a.r;
+  const int head = g * a.r + (rho - t * a.r);
   const int64_t tok = tok0 + t;
-  uint16_t* op = a.out + (tok * a.hq + h) * kHeadDim + 4 * lane;
+  uint16_t* op = a.out + (tok * a.hq + head) * kHeadDim + 4 * lane;
   *reinterpret_cast<uint2*>(op) = make_uint2(pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv));
-  if (lane == 0 && a.lse) a.lse[tok * a.hq + h] = wsum > 0.f ? mx + logf(wsum) : kNegInf;
+  if (lane == 0 && a.lse) a.lse[tok * a.hq + head] = wsum > 0.f ? mx + logf(wsum) : kNegInf;
 }
 
-hipError_t launch_causal(const CausalArgs& a, bool prefill, int q_dtype, int kv_dtype, int gx, int gy, int gz,
-                         hipStream_t s) {
-  dim3 grid(gx, gy, gz), block(256);
-  if (prefill) {
-    if (q_dtype == kFP8 && kv_dtype == kFP8)
-      hipLaunchKernelGGL((causal_kernel<true, kFP8, kFP8>), grid, block, 0, s, a);
-    else if (q_dtype == kBF16 && kv_dtype == kFP8)
-      hipLaunchKernelGGL((causal_kernel<true, kBF16, kFP8>), grid, block, 0, s, a);
-    else
-      hipLaunchKernelGGL((causal_kernel<true, kBF16, kBF16>), grid, block, 0, s, a);
-  } else {
-    if (kv_dtype == kFP8)
-      hipLaunchKernelGGL((causal_kernel<false, kBF16, kFP8>), grid, block, 0, s, a);
-    else
-      hipLaunchKernelGGL((causal_kernel<false, kBF16, kBF16>), grid, block, 0, s, a);
-  }
+hipError_t launch_verify(const VerifyArgs& a, int kv_dtype, int num_wg, hipStream_t s) {
+  if (kv_dtype == kFP8)
+    hipLaunchKernelGGL(verify_kernel<kFP8>, dim3(num_wg), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(verify_kernel<kBF16>, dim3(num_wg), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
-hipError_t launch_merge(const MergeArgs& a, int max_q_len, hipStream_t s) {
-  dim3 grid((max_q_len * a.hq + 3) / 4, a.num_seqs), block(256);
-  hipLaunchKernelGGL(lse_merge_kernel, grid, block, 0, s, a);
+hipError_t launch_verify_merge(const VerifyArgs& a, int num_wg, hipStream_t s) {
+  dim3 grid(a.num_seqs * a.kv.num_kv_heads, (a.rows_cap + 3) / 4);
+  hipLaunchKernelGGL(verify_merge_kernel, grid, dim3(256), 0, s, a, num_wg);
   return hipGetLastError();
 }
 

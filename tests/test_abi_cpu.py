@@ -109,17 +109,28 @@ def test_verify_nothing_to_do_returns_ok_without_launch(lib):
     assert verify(lib, maxk=0) == OK
 
 
+def _ws_expect(hq, hkv, nseq, maxq, maxk, split):
+    # One fp32 slot of r * max_q_len rows x (256 + 1) per (segment, workgroup)
+    # piece: at most #segments + #workgroups of them.
+    tiles = -(-maxk // 64)
+    seg_tiles = split // 64 if split else max(1, tiles)
+    segs = max(1, -(-tiles // seg_tiles))
+    units = nseq * hkv
+    wg_cap = min(1024, max(1, -(-units * tiles // 4)))
+    slots = units * segs + wg_cap
+    rows = hq // hkv * maxq
+    o = slots * rows * 256 * 4
+    return ((o + 255) & ~255) + slots * rows * 4
+
+
 def test_verify_workspace_plan(lib):
-    # One segment: no workspace.  Split segments: fp32 partial rows plus one lse per row.
-    assert pga.verify_workspace_bytes(16, 1, 64, 4, 4096, 1 << 20) == 0
-    split = pga.verify_split_tokens(16, 1, 64, 4, 32768, 0)
-    assert split % 64 == 0 and split >= 512
-    segs = -(-32768 // split)
-    b = pga.verify_workspace_bytes(16, 1, 64, 4, 32768, 0)
-    o = 64 * segs * 64 * 256 * 4
-    assert b == ((o + 255) & ~255) + 64 * segs * 64 * 4
+    for args in [(16, 1, 64, 4, 32768, 0), (32, 2, 128, 3, 65536, 4096), (16, 1, 2, 2, 1000, 0),
+                 (16, 1, 64, 4, 4096, 1 << 20), (8, 1, 3, 4, 64, 64)]:
+        assert pga.verify_workspace_bytes(*args) == _ws_expect(*args), args
+    assert pga.verify_split_tokens(16, 1, 64, 4, 32768, 0) == 32768      # auto: whole history per segment
     assert pga.verify_split_tokens(32, 2, 128, 3, 65536, 4096) == 4096
-    assert pga.verify_workspace_bytes(16, 1, 2, 4, 1000, 100) == 0   # invalid split -> 0
+    assert pga.verify_workspace_bytes(16, 1, 2, 4, 1000, 100) == 0       # invalid split -> 0
+    assert pga.verify_workspace_bytes(16, 1, 0, 4, 1000, 0) == 0         # no sequences
 
 
 def prefill(lib, kv=None, **kw):

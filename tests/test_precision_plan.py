@@ -35,11 +35,39 @@ def _round(x, kind):
     raise ValueError(kind)
 
 
-def emulate(p, p_kind, split=1, partial_kind="f32", tile=64):
+def split_q_fp8(q):
+    """bf16 query rows as an FP8 E4M3 high part plus an FP8 low part scaled by
+    2^4, with a power-of-two row scale putting the row maximum in [128, 256):
+    returns q_hi + q_lo / 16 (in the original units)."""
+    q = np.asarray(q, dtype=np.float64)
+    amax = np.abs(q).max(-1, keepdims=True)
+    e = np.floor(np.log2(np.where(amax > 0, amax, 1.0)))
+    s = 2.0 ** (7 - e)
+    qs = torch.from_numpy((q * s).astype(np.float32))
+    hi = qs.to(torch.float8_e4m3fn).to(torch.float32)
+    lo = ((qs - hi) * 16).to(torch.float8_e4m3fn).to(torch.float32)
+    return ((hi + lo / 16).double() / torch.from_numpy(s)).numpy()
+
+
+def test_fp8_split_of_bf16_q_is_exact_for_gaussian_rows():
+    # The split reproduces every bf16 element whose scaled magnitude is at least
+    # 2^-6, i.e. all but the smallest ~1e-4 of each row's range.
+    rng = np.random.Generator(np.random.PCG64(9))
+    q = torch.from_numpy(rng.standard_normal((512, 256)).astype(np.float32)).to(torch.bfloat16).double().numpy()
+    back = split_q_fp8(q)
+    amax = np.abs(q).max(-1, keepdims=True)
+    big = np.abs(q) >= amax * 2.0 ** -13
+    assert np.array_equal(back[big], q[big])
+    assert np.max(np.abs(back - q)) <= np.max(amax) * 2.0 ** -17
+
+
+def emulate(p, p_kind, split=1, partial_kind="f32", tile=64, q_split=False):
     """Tiled online softmax with the given P rounding; returns bf16-rounded out."""
     T, Hq, D = p.num_tokens, p.num_q_heads, p.head_dim
     r = Hq // p.num_kv_heads
     q = refs.decode_torch(p.q, p.q_dtype).numpy()
+    if q_split:
+        q = split_q_fp8(q.reshape(-1, D)).reshape(q.shape)
     out = np.zeros((T, Hq, D))
     for b in range(p.num_seqs):
         k, v = refs.logical_kv(p, b)
@@ -110,3 +138,11 @@ def test_split_partials_must_stay_fp32(cases):
     p, ref = cases[1]
     assert refs.rel_l2(emulate(p, "fp16", split=4, partial_kind="f32"), ref) < TOL
     assert refs.rel_l2(emulate(p, "fp16", split=4, partial_kind="bf16"), ref) > TOL
+
+
+def test_qk_on_fp8_mfma_with_split_q(cases):
+    # FP8 keys against bf16 queries split into two FP8 parts: same error as bf16 QK.
+    p, ref = cases[1]
+    e_split = refs.rel_l2(emulate(p, "fp16", q_split=True), ref)
+    e_bf16 = refs.rel_l2(emulate(p, "fp16"), ref)
+    assert e_split < TOL and abs(e_split - e_bf16) < 2e-5
