@@ -124,9 +124,10 @@ typedef struct pga_paged_kv {
  *                 shares end); otherwise the longest piece of one history
  *                 that one workgroup attends, a positive multiple of 64
  *   workspace     device buffer of at least paged_attn_verify_workspace_bytes()
- *                 bytes, 256-byte aligned; holds fp32 partial rows and their
- *                 lse values between the two stages; caller-owned, its
- *                 contents on entry do not matter
+ *                 bytes, 256-byte aligned; holds the partial rows (fp16 for
+ *                 FP8 V, fp32 for BF16 V) and their lse values between the
+ *                 two stages; caller-owned, its contents on entry do not
+ *                 matter
  *   out           [T, num_q_heads, 256] bf16;  lse  [T, num_q_heads] fp32 or NULL
  * Returns PGA_OK or a PGA_ERR_* code.
  */

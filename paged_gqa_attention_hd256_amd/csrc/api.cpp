@@ -84,11 +84,14 @@ struct VerifyPlan {
   int32_t max_segs = 0;    // segments per (sequence, kv head), host bound
   int32_t rows_cap = 0;    // r * max_q_len
   int32_t wg_cap = 0;      // bound of the persistent grid (device independent)
-  size_t ws_o_bytes = 0, ws_bytes = 0;
+  size_t ws_o_bytes = 0, ws_lse_bytes = 0, ws_bytes = 0;
 };
 
 // Verify work plan from the host bounds.  The workspace holds one slot per
-// (segment, workgroup) piece: at most #segments + #workgroups of them.
+// (segment, workgroup) piece -- at most #segments + #workgroups of them -- of
+// partial rows and their lse values, then the plan the merge reads: per
+// (sequence, kv head) unit its first tile and first segment in the flattened
+// order, and the tiles per workgroup.
 bool plan_verify(int32_t hq, int32_t hkv, int32_t num_seqs, int32_t max_q_len, int32_t max_kv_len,
                  int32_t kv_split_tokens, VerifyPlan& p) {
   if (hq <= 0 || hkv <= 0 || hq % hkv != 0 || num_seqs < 0 || max_q_len < 1 || max_kv_len < 0) return false;
@@ -104,7 +107,8 @@ bool plan_verify(int32_t hq, int32_t hkv, int32_t num_seqs, int32_t max_q_len, i
     const size_t slots = size_t(units) * p.max_segs + p.wg_cap;
     p.ws_o_bytes = slots * p.rows_cap * kHeadDim * sizeof(float);
     p.ws_o_bytes = (p.ws_o_bytes + 255) & ~size_t(255);
-    p.ws_bytes = p.ws_o_bytes + slots * p.rows_cap * sizeof(float);
+    p.ws_lse_bytes = (slots * p.rows_cap * sizeof(float) + 15) & ~size_t(15);
+    p.ws_bytes = p.ws_o_bytes + p.ws_lse_bytes + (size_t(units) * 2 + 4) * sizeof(int32_t);
   }
   return true;
 }
@@ -199,8 +203,9 @@ static int prepare_verify(const void* q, int32_t q_dtype, const float* q_descale
   a.rows_cap = p.rows_cap;
   a.out = static_cast<uint16_t*>(out);
   a.lse = lse;
-  a.ws_o = static_cast<float*>(workspace);
+  a.ws_o = workspace;
   a.ws_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + p.ws_o_bytes);
+  a.ws_plan = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + p.ws_o_bytes + p.ws_lse_bytes);
   const int occupancy = kv->dtype == kFP8 ? 2 : 1;  // workgroups per CU the LDS allows
   num_wg = std::max(1, std::min(p.wg_cap, device_cus() * occupancy));
   return PGA_OK;
@@ -235,7 +240,7 @@ int paged_attn_verify_merge(const void* q, int32_t q_dtype, const float* q_desca
   bool nothing;
   if (int e = prepare_verify(PGA_VERIFY_ARGS, p, a, num_wg, nothing)) return e;
   if (nothing) return PGA_OK;
-  return launch_status(pga::launch_verify_merge(a, num_wg, static_cast<hipStream_t>(stream)));
+  return launch_status(pga::launch_verify_merge(a, kv->dtype, num_wg, static_cast<hipStream_t>(stream)));
 }
 
 int paged_attn_verify(const void* q, int32_t q_dtype, const float* q_descale, int32_t num_q_heads, int32_t num_seqs,
@@ -250,7 +255,7 @@ int paged_attn_verify(const void* q, int32_t q_dtype, const float* q_descale, in
   if (nothing) return PGA_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (int e = launch_status(pga::launch_verify(a, kv->dtype, num_wg, s))) return e;
-  return launch_status(pga::launch_verify_merge(a, num_wg, s));
+  return launch_status(pga::launch_verify_merge(a, kv->dtype, num_wg, s));
 }
 
 int paged_attn_prefill_prefix(const void* q, int32_t q_dtype, const float* q_descale, int32_t num_q_heads,
@@ -269,7 +274,7 @@ int paged_attn_prefill_prefix(const void* q, int32_t q_dtype, const float* q_des
   if (!aligned(q, 16) || !aligned(out, 8) || (lse && !aligned(lse, 4))) return PGA_ERR_UNSUPPORTED;
   if (num_seqs == 0 || max_seqlen_q == 0) return PGA_OK;
 
-  const int32_t tile_tokens = kMaxRowsPerGroup / r;
+  const int32_t tile_tokens = pga::prefill_tile_tokens(q_dtype, kv->dtype, r);
   const int64_t q_tiles = cdiv(max_seqlen_q, tile_tokens);
   if (q_tiles > INT32_MAX) return PGA_ERR_UNSUPPORTED;
   pga::PrefillArgs a{};

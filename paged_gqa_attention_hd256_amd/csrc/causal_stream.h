@@ -1,12 +1,19 @@
 // Streaming of a contiguous key range of one (sequence, kv head) through LDS,
-// shared by the verify and prefill kernels.
+// shared by the verify and prefill kernels, and the attention of the
+// workgroup's 64 query rows on each streamed tile.
 //
 // A workgroup of four waves walks keys [k_lo, k_hi) in 64-key tiles.  Each
 // wave fetches 16 rows of every tile (K and V) by 16-byte global->LDS DMA into
-// a double buffer, then each wave whose 16 query rows are live runs the
-// attention core on the tile.  The page of a wave's 16 rows is read with a
-// scalar load, so the only vector-memory instructions in flight are the DMA
-// and the wait for tile i can let tile i + 1 stay in flight.
+// a double buffer.  The page of a wave's 16 rows is read with a scalar load, so
+// the only vector-memory instructions in flight are the DMA and the wait for
+// tile i can let tile i + 1 stay in flight.
+//
+// On a tile the work is split two ways.  For QK^T and the softmax, wave w owns
+// query rows 16w .. 16w + 15 (its scores, running maximum and row sum); it
+// publishes the probabilities, already in the B-operand layout of the PV
+// MFMA, and its rows' rescale factors to LDS.  For PV, wave w owns head
+// dimensions 64w .. 64w + 63 of all 64 rows, so each wave reads and widens a
+// quarter of the V tile instead of all of it.
 #pragma once
 
 #include "attn_core.h"
@@ -14,10 +21,29 @@
 
 namespace pga {
 
+// Exchange area between the softmax of a tile and its PV product.
+template <int KV>
+struct Exchange {
+  static constexpr int kPVec = (KV == kFP8) ? 1 : 2;  // 16-byte P fragments per lane: fp16, or bf16 high + low
+  i32x4 p[4][2][kPVec][64];                           // [row block][32-key step][part][lane]
+  float row[64];  // per row: rescale factor of the current tile; at the end, the row sum
+  int grow[4];    // per softmax wave: whether any of its rows was rescaled on this tile
+};
+
 template <int KV>
 struct CausalSmem {
   static constexpr int kTileBytes = TileGeom<KV>::template tile_bytes<64>();
   char buf[2][2][kTileBytes];  // [buffer][K, V]
+  Exchange<KV> x;
+};
+
+// Running maximum (log2 domain) and this lane's partial row sum of one softmax row.
+struct RowStat {
+  float m, l;
+  __device__ __forceinline__ void init() {
+    m = kNegInf;
+    l = 0.f;
+  }
 };
 
 // Uniform load through the scalar data cache (read-only data, uniform address).
@@ -26,82 +52,293 @@ __device__ __forceinline__ T scalar_load(const T* p) {
   return *(const __attribute__((address_space(4))) T*)(p);
 }
 
-// Attend keys [k_lo, k_hi) of kv head g of the sequence whose block-table row
-// is bt_row.  c2: this row's log2-domain score multiplier (including the Q
-// fragment's rscale).  klim: largest visible key of this lane's query row; min_lim: the
-// smallest such limit over the workgroup's rows (tiles entirely at or below it
-// skip the mask).  Every wave of the workgroup must call this (it contains
-// barriers); `compute` is false for waves without live query rows.
-template <int QDT, int KV>
+// Stream keys [k_lo, k_hi) of kv head g of the sequence whose block-table row
+// is bt_row through LDS, calling tile.front(kt, tb) and then tile.back(vt, tb)
+// on every 64-key tile in every wave (kt / vt: the tile's K and V in LDS; tb:
+// its first key).  front may read only K and back only V and the exchange
+// area; a barrier separates them.  Every wave of the workgroup must call this.
+//
+// K and V have separate double buffers: K of tile i + 2 is requested as soon
+// as front(i) is done with K of tile i (about 1.5 tiles ahead), V of tile i + 1
+// as soon as back(i - 1) is done with V of tile i - 1 (one tile ahead), so two
+// barriers per tile suffice and more of the gather is in flight.
+template <int KV, class Tile>
 __device__ __forceinline__ void stream_keys(CausalSmem<KV>& sm, const KvArgs& kv, const int32_t* bt_row, int g,
-                                            int k_lo, int k_hi, const QFragT<KV>& qf, float c2, int klim,
-                                            int min_lim, bool compute, WaveState& st) {
+                                            int k_lo, int k_hi, const Tile& tile) {
   using G = TileGeom<KV>;
   constexpr int kRowsPerDma = 1024 / G::kRowBytes;  // rows one 1 KB DMA instruction fills
-  constexpr int kDmaPerWave = 16 / kRowsPerDma;     // per wave, for its 16 rows of K (or V)
+  constexpr int kDma = 16 / kRowsPerDma;            // per wave, for its 16 rows of K (or V)
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = lane_id();
-  const uint8_t* kbase = kv.k + g * kv.k_sh;
-  const uint8_t* vbase = kv.v + g * kv.v_sh;
   const int ntiles = (k_hi - k_lo + 63) >> 6;
 
   // This wave's rows of a tile (16w .. 16w + 15) lie in one page: pages hold
-  // at least 16 tokens and tiles start at multiples of 64.  The page id of tile
-  // it + 2 is requested while tile it is being computed, so the scalar read
-  // (often a cache miss: block-table rows are long) never delays a DMA issue.
+  // at least 16 tokens and tiles start at multiples of 64.  Page ids are read
+  // with scalar loads two tiles ahead, so the read (often a cache miss:
+  // block-table rows are long) never delays a DMA issue.
   auto page_of = [&](int it) {
     const int key0 = k_lo + it * 64 + 16 * w;
     const int pidx = __builtin_amdgcn_readfirstlane(min(key0, k_hi - 1) >> kv.page_shift);
     return scalar_load(bt_row + pidx);
   };
-  auto issue = [&](int it, int buf, int page) {
+  // kDma DMA instructions per call, whatever the keys (absent keys read zeros).
+  auto issue = [&](int it, int page, const uint8_t* base, int64_t sh, int64_t sp, int64_t st, char* dst) {
     const int tb = k_lo + it * 64;
     const bool page_ok = page >= 0 && page < kv.num_pages;
-    const int64_t kpage = (int64_t)page * kv.k_sp;
-    const int64_t vpage = (int64_t)page * kv.v_sp;
+    const uint8_t* pbase = base + g * sh + (int64_t)page * sp;
 #pragma unroll
-    for (int u = 0; u < kDmaPerWave; ++u) {
+    for (int u = 0; u < kDma; ++u) {
       const int row0 = 16 * w + u * kRowsPerDma;
       const int row = row0 + lane / G::kChunks;
       const int chunk = (lane % G::kChunks) ^ (row & (G::kChunks - 1));
       const int key = tb + row;
       const bool ok = page_ok && key < k_hi;
-      const int slot = key & (kv.page_size - 1);
-      const uint8_t* ks = ok ? kbase + kpage + slot * kv.k_st + chunk * 16 : reinterpret_cast<const uint8_t*>(g_zero16);
-      const uint8_t* vs = ok ? vbase + vpage + slot * kv.v_st + chunk * 16 : reinterpret_cast<const uint8_t*>(g_zero16);
-      dma16(ks, (lds_t*)&sm.buf[buf][0][row0 * G::kRowBytes]);
-      dma16(vs, (lds_t*)&sm.buf[buf][1][row0 * G::kRowBytes]);
+      const uint8_t* src = ok ? pbase + (key & (kv.page_size - 1)) * st + chunk * 16
+                              : reinterpret_cast<const uint8_t*>(g_zero16);
+      dma16(src, (lds_t*)(dst + row0 * G::kRowBytes));
     }
   };
+  auto issue_k = [&](int it, int page) { issue(it, page, kv.k, kv.k_sh, kv.k_sp, kv.k_st, &sm.buf[it & 1][0][0]); };
+  auto issue_v = [&](int it, int page) { issue(it, page, kv.v, kv.v_sh, kv.v_sp, kv.v_st, &sm.buf[it & 1][1][0]); };
 
   if (ntiles <= 0) return;
-  issue(0, 0, page_of(0));
-  int next_page = ntiles > 1 ? page_of(1) : 0;
+  const int pg0 = page_of(0);
+  issue_k(0, pg0);
+  issue_v(0, pg0);
+  int pg1 = ntiles > 1 ? page_of(1) : 0;  // page of tile it + 1
+  if (ntiles > 1) {
+    issue_k(1, pg1);
+    issue_v(1, pg1);
+  }
   for (int it = 0; it < ntiles; ++it) {
-    const int after_page = it + 2 < ntiles ? page_of(it + 2) : 0;
-    if (it + 1 < ntiles) {
-      issue(it + 1, (it + 1) & 1, next_page);
-      wait_vmcnt<2 * kDmaPerWave>();
+    const int pg2 = it + 2 < ntiles ? page_of(it + 2) : 0;
+    // DMA issue order: ..., K(it) V(it) | then K(it + 1) (and, at it = 0, V(1)).
+    if (it == 0) {
+      if (ntiles > 1) wait_vmcnt<2 * kDma>(); else wait_vmcnt<0>();
     } else {
-      wait_vmcnt<0>();
+      if (it + 1 < ntiles) wait_vmcnt<kDma>(); else wait_vmcnt<0>();
     }
-    next_page = after_page;
-    barrier();
-    if (compute) {
-      const lds_t* kt = (const lds_t*)&sm.buf[it & 1][0][0];
-      const lds_t* vt = (const lds_t*)&sm.buf[it & 1][1][0];
-      const int tb = k_lo + it * 64;
+    barrier();  // tile it is in LDS; every wave is done with back(it - 1)
+    if (it >= 1 && it + 1 < ntiles) issue_v(it + 1, pg1);
+    const int tb = k_lo + it * 64;
+    tile.front((const lds_t*)&sm.buf[it & 1][0][0], tb);
+    barrier_publish();  // every wave is done with K of tile it; the exchange area is complete
+    if (it + 2 < ntiles) issue_k(it + 2, pg2);
+    tile.back((const lds_t*)&sm.buf[it & 1][1][0], tb);
+    pg1 = pg2;
+  }
+}
+
+// Softmax of this wave's 16 rows on a tile (scores s from tile_scores), as
+// tile_softmax does it, except that the rescale factor is published for the PV
+// waves instead of being applied, and the probabilities go to LDS as PV
+// operands.
+template <int KV, bool MASKED, class Vis>
+__device__ __forceinline__ void softmax_publish(RowStat& rs, f32x4 (&s)[4], float c2, Vis visible,
+                                                Exchange<KV>& x, int w) {
+  const int lane = lane_id();
+  const int gq = lane >> 4, n = lane & 15;
+  float mt = kNegInf;
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float v = s[mb][i] * c2;
+      if constexpr (MASKED) v = visible(mb * 16 + 4 * gq + i) ? v : kNegInf;
+      s[mb][i] = v;
+      mt = fmaxf(mt, v);
+    }
+  }
+  mt = group4_max(mt);
+  const uint64_t grow = __builtin_amdgcn_ballot_w64(mt > rs.m + kRescaleLog2);
+  float alpha = 1.f;
+  if (grow != 0) {  // wave-uniform
+    const float m_new = fmaxf(rs.m, mt);
+    alpha = m_new == rs.m ? 1.f : fast_exp2(rs.m - m_new);
+    rs.l *= alpha;
+    rs.m = m_new;
+  }
+  const float m_use = (rs.m == kNegInf) ? 0.f : rs.m;
+  float sum = 0.f;
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float p = fast_exp2(s[mb][i] - m_use);
+      s[mb][i] = p;
+      sum += p;
+    }
+  }
+  rs.l += sum;
+  if (gq == 0) x.row[16 * w + n] = alpha;
+  if (lane == 0) x.grow[w] = grow != 0;
+  // B operand of the 32-key step t: keys 32t + 4gq + i and 32t + 16 + 4gq + i.
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    if constexpr (KV == kFP8) {
+      const f16x8 pb = {(_Float16)s[2 * t][0],     (_Float16)s[2 * t][1],     (_Float16)s[2 * t][2],
+                        (_Float16)s[2 * t][3],     (_Float16)s[2 * t + 1][0], (_Float16)s[2 * t + 1][1],
+                        (_Float16)s[2 * t + 1][2], (_Float16)s[2 * t + 1][3]};
+      x.p[w][t][0][lane] = __builtin_bit_cast(i32x4, pb);
+    } else {
+      bf16x8 ph, pl;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float v = s[2 * t + (j >> 2)][j & 3];
+        const __bf16 h = (__bf16)v;
+        ph[j] = h;
+        pl[j] = (__bf16)(v - (float)h);
+      }
+      x.p[w][t][0][lane] = __builtin_bit_cast(i32x4, ph);
+      x.p[w][t][1][lane] = __builtin_bit_cast(i32x4, pl);
+    }
+  }
+}
+
+// A wave without live query rows: zero probabilities and no rescale.
+template <int KV>
+__device__ __forceinline__ void publish_nothing(Exchange<KV>& x, int w) {
+  const int lane = lane_id();
+  if (lane < 16) x.row[16 * w + lane] = 1.f;
+  if (lane == 0) x.grow[w] = 0;
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int c = 0; c < Exchange<KV>::kPVec; ++c) x.p[w][t][c][lane] = i32x4{0, 0, 0, 0};
+}
+
+// O^T += V^T P^T for head dimensions 64w .. 64w + 63 of all 64 rows, after
+// applying the published rescale factors: o[4 * rb + db] holds rows
+// 16rb + lane % 16 and dims 64w + 16db + 4 (lane / 16) + i.
+template <int KV>
+__device__ __forceinline__ void pv_quarter(f32x4 (&o)[16], const lds_t* vt, const Exchange<KV>& x, int w) {
+  using G = TileGeom<KV>;
+  const int lane = lane_id();
+  const int gq = lane >> 4, sl = lane & 15;
+  const int any = x.grow[0] | x.grow[1] | x.grow[2] | x.grow[3];
+  if (__builtin_amdgcn_readfirstlane(any) != 0) {
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+      const float al = x.row[16 * rb + sl];
+#pragma unroll
+      for (int db = 0; db < 4; ++db) o[4 * rb + db] *= al;
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    if constexpr (KV == kFP8) {
+      f16x8 pb[4];
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) pb[rb] = __builtin_bit_cast(f16x8, x.p[rb][t][0][lane]);
+      // transpose-read source: lane sl = 2e + q points at key(e), bytes 8q..8q+7 of the d-block
+      const int e = sl >> 1, q = sl & 1;
+      const int key = 32 * t + 16 * (e >> 2) + 4 * gq + (e & 3);
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        const f16x8 a = fp8x8_to_f16(lds_tr8(vt + G::off(key, 4 * w + db) + 8 * q));
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb) o[4 * rb + db] = mfma_f16(a, pb[rb], o[4 * rb + db]);
+      }
+    } else {
+      bf16x8 ph[4], pl[4];
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) {
+        ph[rb] = __builtin_bit_cast(bf16x8, x.p[rb][t][0][lane]);
+        pl[rb] = __builtin_bit_cast(bf16x8, x.p[rb][t][1][lane]);
+      }
+      // transpose-read source: lane sl = 4e + q points at key(e), columns 4q..4q+3
+      const int e = sl >> 2, q = sl & 3;
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        const int chunk = 2 * (4 * w + db) + (q >> 1);
+        const int key0 = 32 * t + 4 * gq + e;
+        const i32x2 lo = __builtin_bit_cast(i32x2, lds_tr16(vt + G::off(key0, chunk) + 8 * (q & 1)));
+        const i32x2 hi = __builtin_bit_cast(i32x2, lds_tr16(vt + G::off(key0 + 16, chunk) + 8 * (q & 1)));
+        const bf16x8 a = __builtin_bit_cast(bf16x8, i32x4{lo[0], lo[1], hi[0], hi[1]});
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb) {
+          o[4 * rb + db] = mfma_bf16(a, ph[rb], o[4 * rb + db]);
+          o[4 * rb + db] = mfma_bf16(a, pl[rb], o[4 * rb + db]);
+        }
+      }
+    }
+  }
+}
+
+// The workgroup's 64 rows on one streamed tile.  qf, c2, klim, rs: this wave's
+// softmax rows (c2 includes the Q fragment's rscale; klim is the largest
+// visible key of this lane's row); min_lim: the smallest such limit over the
+// workgroup's rows (tiles entirely at or below it skip the mask); live: this
+// wave has live softmax rows; o: this wave's PV quarter.
+template <int QDT, int KV>
+struct SplitTile {
+  const QFragT<KV>& qf;
+  float c2;
+  int klim, min_lim;
+  bool live;
+  RowStat& rs;
+  f32x4 (&o)[16];
+  Exchange<KV>& x;
+  __device__ __forceinline__ void front(const lds_t* kt, int tb) const {
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (live) {
       f32x4 sc[4];
       tile_scores<KV, 4, QDT == kBF16>(kt, qf, sc);
       const int lim = klim - tb;
       if (tb + 63 > min_lim)  // workgroup-uniform: only tiles past the first row's diagonal or the range end
-        tile_softmax<true>(st, sc, c2, [lim](int key) { return key <= lim; });
+        softmax_publish<KV, true>(rs, sc, c2, [lim](int key) { return key <= lim; }, x, w);
       else
-        tile_softmax<false>(st, sc, c2, [](int) { return true; });
-      tile_pv<KV, 4>(st, vt, sc);
+        softmax_publish<KV, false>(rs, sc, c2, [](int) { return true; }, x, w);
+    } else {
+      publish_nothing(x, w);
     }
-    barrier();
   }
+  __device__ __forceinline__ void back(const lds_t* vt, int) const {
+    pv_quarter<KV>(o, vt, x, __builtin_amdgcn_readfirstlane(threadIdx.x >> 6));
+  }
+};
+
+// After the last tile: each softmax wave publishes its rows' sums (0 for a wave
+// without live rows) so that every wave can normalise its PV quarter; returns
+// this lane's row sum.  Contains a barrier.
+template <int KV>
+__device__ __forceinline__ float finish_rows(const RowStat& rs, bool live, Exchange<KV>& x) {
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = lane_id();
+  const float lrow = live ? group4_sum(rs.l) : 0.f;
+  if (lane < 16) x.row[16 * w + lane] = lrow;
+  barrier_publish();
+  return lrow;
+}
+
+// Row rb of this wave's PV quarter times `scale`, written to a row of 256
+// head dimensions: bf16 (output) or fp32 (partial).
+__device__ __forceinline__ void store_quarter_bf16(const f32x4 (&o)[16], int rb, float scale, uint16_t* row_base) {
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int gq = lane_id() >> 4;
+#pragma unroll
+  for (int db = 0; db < 4; ++db) {
+    const f32x4 v = o[4 * rb + db];
+    *reinterpret_cast<uint2*>(row_base + 64 * w + 16 * db + 4 * gq) =
+        make_uint2(pack_bf16x2(v[0] * scale, v[1] * scale), pack_bf16x2(v[2] * scale, v[3] * scale));
+  }
+}
+__device__ __forceinline__ void store_quarter_f16(const f32x4 (&o)[16], int rb, float scale, uint16_t* row_base) {
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int gq = lane_id() >> 4;
+#pragma unroll
+  for (int db = 0; db < 4; ++db) {
+    const f32x4 v = o[4 * rb + db] * scale;
+    const f16x4 h = {(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
+    *reinterpret_cast<f16x4*>(row_base + 64 * w + 16 * db + 4 * gq) = h;
+  }
+}
+__device__ __forceinline__ void store_quarter_f32(const f32x4 (&o)[16], int rb, float scale, float* row_base) {
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int gq = lane_id() >> 4;
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+    *reinterpret_cast<f32x4*>(row_base + 64 * w + 16 * db + 4 * gq) = o[4 * rb + db] * scale;
 }
 
 // Q^T fragment of this lane's query row (lane % 16 of the wave), complete on
@@ -178,21 +415,6 @@ __device__ __forceinline__ void load_q(QFragT<KV>& qf, const void* q, int64_t to
     }
   }
   wait_vmcnt<0>();
-}
-
-// Final bf16 output row (and lse) of one wave's query row from its state.
-__device__ __forceinline__ void store_out(const WaveState& st, float lrow, float vds, uint16_t* out, float* lse,
-                                          int64_t tok, int hq, int head) {
-  const int gq = lane_id() >> 4;
-  const float inv = lrow > 0.f ? vds / lrow : 0.f;
-  uint16_t* op = out + (tok * hq + head) * kHeadDim + 4 * gq;
-#pragma unroll
-  for (int mb = 0; mb < 16; ++mb) {
-    const uint32_t lo = pack_bf16x2(st.o[mb][0] * inv, st.o[mb][1] * inv);
-    const uint32_t hi = pack_bf16x2(st.o[mb][2] * inv, st.o[mb][3] * inv);
-    *reinterpret_cast<uint2*>(op + 16 * mb) = make_uint2(lo, hi);
-  }
-  if (gq == 0 && lse) lse[tok * hq + head] = lrow > 0.f ? (st.m + log2f(lrow)) * kLn2 : kNegInf;
 }
 
 }  // namespace pga

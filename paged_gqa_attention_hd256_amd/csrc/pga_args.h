@@ -39,8 +39,10 @@ struct VerifyArgs {
   int32_t rows_cap;        // r * max_q_len: row slots per workspace slot
   uint16_t* out;           // [T, hq, 256] bf16
   float* lse;              // [T, hq] or null
-  float* ws_o;             // [slots, rows_cap, 256] fp32 partial outputs (normalised, v-descaled)
+  void* ws_o;              // [slots, rows_cap, 256] partial outputs divided by their row sums, in V code
+                           // units (v_descale not applied): fp16 for FP8 V (|x| <= 448), fp32 for BF16 V
   float* ws_lse;           // [slots, rows_cap] fp32 natural-log lse of the partials
+  int32_t* ws_plan;        // [units][2]: first tile, first segment of each unit; then tiles per workgroup
 };
 
 // Prefill against a cached prefix: one workgroup per (tile of query tokens,
@@ -76,7 +78,9 @@ struct SparseArgs {
 
 // Launchers (defined next to their kernels).  They return the launch status.
 hipError_t launch_verify(const VerifyArgs& a, int kv_dtype, int num_wg, hipStream_t s);
-hipError_t launch_verify_merge(const VerifyArgs& a, int num_wg, hipStream_t s);
+hipError_t launch_verify_merge(const VerifyArgs& a, int kv_dtype, int num_wg, hipStream_t s);
+// Query tokens per prefill workgroup for this dtype pair and group size r.
+int prefill_tile_tokens(int q_dtype, int kv_dtype, int r);
 hipError_t launch_prefill(const PrefillArgs& a, int q_dtype, int kv_dtype, int q_tiles, hipStream_t s);
 hipError_t launch_sparse(const SparseArgs& a, int kv_dtype, hipStream_t s);
 

@@ -64,6 +64,15 @@ __device__ __forceinline__ void barrier() {
   asm volatile("" ::: "memory");
 }
 
+// Barrier after which this wave's LDS writes are visible to the other waves:
+// waits for its LDS (and scalar-memory) operations, not for vector memory.
+__device__ __forceinline__ void barrier_publish() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4));  // lgkmcnt(0); vmcnt, expcnt unconstrained
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // 16-byte global -> LDS copy; `lds_wave_base` must be the same for the whole
 // wave (lane l writes lds_wave_base + 16 * l).  Issued from inline assembly so
 // the compiler does not treat every later LDS read as possibly aliasing the

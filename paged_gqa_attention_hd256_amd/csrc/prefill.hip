@@ -9,6 +9,8 @@
 // commit).  Workgroups are ordered longest first.
 #include "causal_stream.h"
 
+
+
 namespace pga {
 
 template <int QDT, int KV>
@@ -27,25 +29,45 @@ __global__ __launch_bounds__(256, (KV == kFP8) ? 2 : 1) void prefill_kernel(Pref
 
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = lane_id();
-  const int rho = 16 * w + (lane & 15);
+  const int n = lane & 15;
+  const int rho = 16 * w + n;  // this lane's softmax row
   const bool row_ok = rho < rows;
   const int tq = row_ok ? rho / a.r : 0;
-  const int t = t_lo + tq;
   const int head = g * a.r + (row_ok ? rho - tq * a.r : 0);
-  const int64_t tok = tok0 + t;
+  const int64_t tok = tok0 + t_lo + tq;
   QFragT<KV> qf;
   load_q<QDT, KV>(qf, a.q, tok, a.hq, head, row_ok);
   const float c2 = a.c2_base * load_scale(a.q_ds) * load_scale(a.kv.k_ds);
-  const int klim = row_ok ? min(lk - lq + t, k_hi - 1) : -1;
+  const int klim = row_ok ? min(lk - lq + t_lo + tq, k_hi - 1) : -1;
   const int min_lim = min(lk - lq + t_lo, k_hi - 1);
-  WaveState st;
-  st.init();
-  const bool active = 16 * w < rows;
-  stream_keys<QDT, KV>(sm, a.kv, a.kv.bt + (int64_t)b * a.kv.bt_stride, g, 0, k_hi, qf, c2 * qf.rscale, klim,
-                       min_lim, active, st);
-  if (!active) return;
-  const float lrow = group4_sum(st.l);
-  if (row_ok) store_out(st, lrow, load_scale(a.kv.v_ds), a.out, a.lse, tok, a.hq, head);
+  const bool live = 16 * w < rows;
+  RowStat rs;
+  rs.init();
+  f32x4 o[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  stream_keys(sm, a.kv, a.kv.bt + (int64_t)b * a.kv.bt_stride, g, 0, k_hi,
+              SplitTile<QDT, KV>{qf, c2 * qf.rscale, klim, min_lim, live, rs, o, sm.x});
+  const float lrow = finish_rows(rs, live, sm.x);
+  if (row_ok && (lane >> 4) == 0 && a.lse)
+    a.lse[tok * a.hq + head] = lrow > 0.f ? (rs.m + log2f(lrow)) * kLn2 : kNegInf;
+  const float vds = load_scale(a.kv.v_ds);
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb) {
+    const int rr = 16 * rb + n;
+    if (rr < rows) {
+      const int t2 = rr / a.r;
+      const float l = sm.x.row[rr];
+      store_quarter_bf16(o, rb, l > 0.f ? vds / l : 0.f,
+                         a.out + ((tok0 + t_lo + t2) * (int64_t)a.hq + g * a.r + rr - t2 * a.r) * kHeadDim);
+    }
+  }
+}
+
+int prefill_tile_tokens(int q_dtype, int kv_dtype, int r) {
+  (void)q_dtype;
+  (void)kv_dtype;
+  return r > 0 ? 64 / r : 0;
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, int q_dtype, int kv_dtype, int q_tiles, hipStream_t s) {

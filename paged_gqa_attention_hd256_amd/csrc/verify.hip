@@ -136,9 +136,14 @@ __global__ __launch_bounds__(256, (KV == kFP8) ? 2 : 1) void verify_kernel(Verif
   const float c2 = a.c2_base * load_scale(a.q_ds) * load_scale(a.kv.k_ds);
   const float vds = load_scale(a.kv.v_ds);
 
+  if (wg == 0 && threadIdx.x == 0) a.ws_plan[2 * a.num_seqs * hkv] = tpw;
   int cur = t0;
   while (cur < t1) {
     const int lt0 = cur - tu;
+    if (lt0 == 0 && threadIdx.x == 0) {  // this workgroup starts the unit: record where it lies
+      a.ws_plan[2 * (b * hkv + g)] = tu;
+      a.ws_plan[2 * (b * hkv + g) + 1] = su;
+    }
     const int s = lt0 / a.seg_tiles;
     const int lts1 = min((s + 1) * a.seg_tiles, sw.tiles);
     const int lt1 = min(lts1, t1 - tu);
@@ -146,34 +151,51 @@ __global__ __launch_bounds__(256, (KV == kFP8) ? 2 : 1) void verify_kernel(Verif
     const int lq = min(scalar_load(a.cu_q + b + 1) - tok0, a.max_q_len);
     const int lk = min(scalar_load(a.lens_k + b), a.max_kv_len);
     const int rows = min(a.r * lq, a.rows_cap);
-    const int rho = 16 * w + n;
+    const int rho = 16 * w + n;  // this lane's softmax row
     const bool row_ok = rho < rows;
     const int t = row_ok ? rho / a.r : 0;
     const int head = g * a.r + (row_ok ? rho - t * a.r : 0);
     const int64_t tok = tok0 + t;
-    const bool wave_active = 16 * w < rows;
+    const bool live = 16 * w < rows;
     QFragT<KV> qf;
     load_q<kBF16, KV>(qf, a.q, tok, a.hq, head, row_ok);
     const int k_lo = lt0 * 64, k_hi = min(lt1 * 64, lk);
     const int klim = row_ok ? min(lk - lq + t, k_hi - 1) : -1;
     const int min_lim = min(lk - lq, k_hi - 1);
-    WaveState st;
-    st.init();
-    stream_keys<kBF16, KV>(sm, a.kv, a.kv.bt + (int64_t)b * a.kv.bt_stride, g, k_lo, k_hi, qf, c2 * qf.rscale,
-                           klim, min_lim, wave_active, st);
-    if (wave_active) {
-      const float lrow = group4_sum(st.l);
-      const bool whole = lt0 == s * a.seg_tiles && lt1 == lts1;
-      if (row_ok) {
-        if (whole && sw.segs == 1) {
-          store_out(st, lrow, vds, a.out, a.lse, tok, a.hq, head);
-        } else {
-          const int64_t slot = (int64_t)su + s + wg;
-          const float inv = lrow > 0.f ? vds / lrow : 0.f;
-          float* wp = a.ws_o + (slot * a.rows_cap + rho) * kHeadDim + 4 * gq;
+    RowStat rs;
+    rs.init();
+    f32x4 o[16];
 #pragma unroll
-          for (int mb = 0; mb < 16; ++mb) *reinterpret_cast<f32x4*>(wp + 16 * mb) = st.o[mb] * inv;
-          if (gq == 0) a.ws_lse[slot * a.rows_cap + rho] = lrow > 0.f ? (st.m + log2f(lrow)) * kLn2 : kNegInf;
+    for (int i = 0; i < 16; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    stream_keys(sm, a.kv, a.kv.bt + (int64_t)b * a.kv.bt_stride, g, k_lo, k_hi,
+                SplitTile<kBF16, KV>{qf, c2 * qf.rscale, klim, min_lim, live, rs, o, sm.x});
+    const float lrow = finish_rows(rs, live, sm.x);
+    // A run that covers a whole uncut unit writes the output; any other piece
+    // writes its normalised fp32 rows and their lse to its workspace slot.
+    const bool direct = lt0 == s * a.seg_tiles && lt1 == lts1 && sw.segs == 1;
+    const int64_t slot = (int64_t)su + s + wg;
+    if (row_ok && gq == 0) {
+      const float lse = lrow > 0.f ? (rs.m + log2f(lrow)) * kLn2 : kNegInf;
+      if (!direct)
+        a.ws_lse[slot * a.rows_cap + rho] = lse;
+      else if (a.lse)
+        a.lse[tok * a.hq + head] = lse;
+    }
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+      const int rr = 16 * rb + n;
+      if (rr < rows) {
+        const float l = sm.x.row[rr];
+        const float inv = l > 0.f ? vds / l : 0.f;
+        if (direct) {
+          const int t2 = rr / a.r;
+          store_quarter_bf16(o, rb, inv, a.out + ((tok0 + t2) * (int64_t)a.hq + g * a.r + rr - t2 * a.r) * kHeadDim);
+        } else if constexpr (KV == kFP8) {
+          store_quarter_f16(o, rb, l > 0.f ? 1.f / l : 0.f,
+                            static_cast<uint16_t*>(a.ws_o) + (slot * a.rows_cap + rr) * kHeadDim);
+        } else {
+          store_quarter_f32(o, rb, l > 0.f ? 1.f / l : 0.f,
+                            static_cast<float*>(a.ws_o) + (slot * a.rows_cap + rr) * kHeadDim);
         }
       }
     }
@@ -193,10 +215,26 @@ __global__ __launch_bounds__(256, (KV == kFP8) ? 2 : 1) void verify_kernel(Verif
   }
 }
 
-// One wave per (unit, query row): the pieces of every segment of the unit, as
-// laid out by verify_kernel, combined with log-sum-exp weights.  Pieces with
-// lse = -inf (no visible key) contribute nothing.
-__global__ __launch_bounds__(256) void verify_merge_kernel(VerifyArgs a, int num_wg) {
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
+  return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off);
+  return x;
+}
+
+// Log-sum-exp merge of the partial rows of every (sequence, kv head) unit that
+// verify_kernel did not write directly.  One wave per query row: the lanes
+// take one piece each (the lse of up to 64 pieces in one load, their maximum
+// and weight sum by wave reductions), then the whole wave reads the pieces'
+// rows with the loads of several pieces in flight at once; batches of 64
+// pieces are combined online.  Pieces with lse = -inf (no visible key) get
+// weight 0.
+template <int KV>
+__global__ __launch_bounds__(256) void verify_merge_kernel(VerifyArgs a) {
   const int hkv = a.kv.num_kv_heads;
   const int u = blockIdx.x;
   const int b = u / hkv, g = u - (u / hkv) * hkv;
@@ -204,35 +242,77 @@ __global__ __launch_bounds__(256) void verify_merge_kernel(VerifyArgs a, int num
   const int lane = lane_id();
   const SeqWork sw = seq_work(a, b);
   if (sw.tiles == 0) return;
-  const int tok0 = a.cu_q[b];
-  const int lq = min(a.cu_q[b + 1] - tok0, a.max_q_len);
+  const int tok0 = scalar_load(a.cu_q + b);
+  const int lq = min(scalar_load(a.cu_q + b + 1) - tok0, a.max_q_len);
   if (rho >= min(a.r * lq, a.rows_cap)) return;
-  const PlanPos p = plan_scan(a, num_wg, 0, b);
-  const int tu = p.tile_prefix * hkv + g * sw.tiles;
-  const int su = p.seg_prefix * hkv + g * sw.segs;
-  if (sw.segs == 1 && tu / p.tpw == (tu + sw.tiles - 1) / p.tpw) return;  // written directly
-  float mx = kNegInf;
-  for (int s = 0; s < sw.segs; ++s) {
-    const int ts0 = tu + s * a.seg_tiles, ts1 = tu + min((s + 1) * a.seg_tiles, sw.tiles);
-    for (int wk = ts0 / p.tpw; wk <= (ts1 - 1) / p.tpw; ++wk)
-      mx = fmaxf(mx, a.ws_lse[((int64_t)su + s + wk) * a.rows_cap + rho]);
-  }
+  // Where the unit lies in the flattened order, as verify_kernel recorded it.
+  const int tu = scalar_load(a.ws_plan + 2 * u);
+  const int su = scalar_load(a.ws_plan + 2 * u + 1);
+  const int tpw = scalar_load(a.ws_plan + 2 * a.num_seqs * hkv);
+  if (sw.segs == 1 && tu / tpw == (tu + sw.tiles - 1) / tpw) return;  // written directly
+  // Pieces per segment: lane s takes segment s (up to 64 segments at once),
+  // so piece j's segment is found by comparisons against a prefix sum instead
+  // of a division per segment per piece.
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  float wsum = 0.f;
-  if (mx != kNegInf) {
-    for (int s = 0; s < sw.segs; ++s) {
-      const int ts0 = tu + s * a.seg_tiles, ts1 = tu + min((s + 1) * a.seg_tiles, sw.tiles);
-      for (int wk = ts0 / p.tpw; wk <= (ts1 - 1) / p.tpw; ++wk) {
-        const int64_t slot = (int64_t)su + s + wk;
-        const float ls = a.ws_lse[slot * a.rows_cap + rho];
-        if (ls == kNegInf) continue;
-        const float wgt = __expf(ls - mx);
-        wsum += wgt;
-        acc += wgt * *reinterpret_cast<const f32x4*>(a.ws_o + (slot * a.rows_cap + rho) * kHeadDim + 4 * lane);
+  float mx = kNegInf, wsum = 0.f;
+  for (int s0 = 0; s0 < sw.segs; s0 += 64) {
+    const int sl = s0 + lane;
+    int first = 0, cnt = 0;
+    if (sl < sw.segs) {
+      first = (tu + sl * a.seg_tiles) / tpw;
+      cnt = (tu + min((sl + 1) * a.seg_tiles, sw.tiles) - 1) / tpw - first + 1;
+    }
+    const int incl = wave_incl_scan(cnt);
+    const int excl = incl - cnt;
+    const int nseg = min(64, sw.segs - s0);
+    const int np = __shfl(incl, nseg - 1);  // pieces of these segments
+    for (int c = 0; c < np; c += 64) {
+      const int j = c + lane;
+      int sj = 0;
+      for (int k = 1; k < nseg; ++k) sj = j >= __builtin_amdgcn_readlane(excl, k) ? k : sj;
+      const int slot = j < np ? su + s0 + sj + __shfl(first, sj) + (j - __shfl(excl, sj)) : -1;
+      const float ls = slot >= 0 ? a.ws_lse[(int64_t)slot * a.rows_cap + rho] : kNegInf;
+      // Online merge of this batch of pieces into (mx, wsum, acc).
+      const float mb = wave_max(ls);
+      if (mb == kNegInf) continue;
+      const float m_new = fmaxf(mx, mb);
+      const float scale = mx == kNegInf ? 0.f : __expf(mx - m_new);
+      acc *= scale;
+      wsum *= scale;
+      mx = m_new;
+      const float wgt = ls == kNegInf ? 0.f : __expf(ls - mx);
+      wsum += wave_sum(wgt);
+      // This lane's 4 head dimensions of the row in piece slot sl.
+      auto part = [&](int sl) -> f32x4 {
+        const int64_t off = ((int64_t)sl * a.rows_cap + rho) * kHeadDim + 4 * lane;
+        if constexpr (KV == kFP8) {
+          const f16x4 h = *reinterpret_cast<const f16x4*>(static_cast<const uint16_t*>(a.ws_o) + off);
+          return f32x4{(float)h[0], (float)h[1], (float)h[2], (float)h[3]};
+        } else {
+          return *reinterpret_cast<const f32x4*>(static_cast<const float*>(a.ws_o) + off);
+        }
+      };
+      // Rows of 8 pieces in flight at a time; past the last piece the weight
+      // is 0 and the slot repeats the last one, so the loads stay in bounds.
+      const int n = min(64, np - c);
+      const int last = __builtin_amdgcn_readlane(slot, n - 1);
+      for (int q = 0; q < n; q += 8) {
+        f32x4 v[8];
+        float wq[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const int src = min(q + k, 63);
+          const int sl = __builtin_amdgcn_readlane(slot, src);
+          wq[k] = q + k < n ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wgt), src)) : 0.f;
+          v[k] = part(q + k < n ? sl : last);
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+          if (wq[k] != 0.f) acc += wq[k] * v[k];
       }
     }
   }
-  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+  const float inv = wsum > 0.f ? load_scale(a.kv.v_ds) / wsum : 0.f;
   const int t = rho / a.r;
   const int head = g * a.r + (rho - t * a.r);
   const int64_t tok = tok0 + t;
@@ -249,9 +329,12 @@ hipError_t launch_verify(const VerifyArgs& a, int kv_dtype, int num_wg, hipStrea
   return hipGetLastError();
 }
 
-hipError_t launch_verify_merge(const VerifyArgs& a, int num_wg, hipStream_t s) {
+hipError_t launch_verify_merge(const VerifyArgs& a, int kv_dtype, int num_wg, hipStream_t s) {
   dim3 grid(a.num_seqs * a.kv.num_kv_heads, (a.rows_cap + 3) / 4);
-  hipLaunchKernelGGL(verify_merge_kernel, grid, dim3(256), 0, s, a, num_wg);
+  if (kv_dtype == kFP8)
+    hipLaunchKernelGGL(verify_merge_kernel<kFP8>, grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(verify_merge_kernel<kBF16>, grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -110,8 +110,8 @@ def test_verify_nothing_to_do_returns_ok_without_launch(lib):
 
 
 def _ws_expect(hq, hkv, nseq, maxq, maxk, split):
-    # One fp32 slot of r * max_q_len rows x (256 + 1) per (segment, workgroup)
-    # piece: at most #segments + #workgroups of them.
+    # One slot of r * max_q_len rows x (256 + 1) fp32 values per (segment,
+    # workgroup) piece -- at most #segments + #workgroups of them.
     tiles = -(-maxk // 64)
     seg_tiles = split // 64 if split else max(1, tiles)
     segs = max(1, -(-tiles // seg_tiles))
@@ -120,7 +120,8 @@ def _ws_expect(hq, hkv, nseq, maxq, maxk, split):
     slots = units * segs + wg_cap
     rows = hq // hkv * maxq
     o = slots * rows * 256 * 4
-    return ((o + 255) & ~255) + slots * rows * 4
+    lse = (slots * rows * 4 + 15) & ~15
+    return ((o + 255) & ~255) + lse + (units * 2 + 4) * 4  # then the per-unit plan and tiles per workgroup
 
 
 def test_verify_workspace_plan(lib):
