@@ -2,19 +2,20 @@
 // log-sum-exp merge kernel.
 //
 // All r * Lq_b query rows of a kv group (token-major: row = t * r + h) sit in
-// one workgroup, 16 rows per wave, so every KV page is fetched from HBM once
-// for all speculative tokens of the group -- the reuse SGLang PR #36330 adds
+// one workgroup, so every KV page is fetched from HBM once for all
+// speculative tokens of the group -- the reuse SGLang PR #36330 adds
 // (Motivation; Modifications: BLOCK_M = 16 x BLOCK_Q).
 //
 // Work split.  The 64-key tiles of every (sequence, kv head) unit, each unit
 // optionally cut into segments of at most kv_split_tokens keys, are laid end to
-// end; a persistent grid of P workgroups takes equal contiguous runs of that
-// list (stream-K).  A run that covers a whole single-segment unit writes the
-// bf16 output directly; any other piece (segment sigma, workgroup w) writes its
-// fp32 partial output, already divided by its row sums, and natural-log lse to
-// workspace slot sigma + w.  Pieces are ordered in both sigma and w, so that
-// slot is unique, and there are at most (#segments + P) of them.  The merge
-// kernel recomputes the same plan and combines each row's pieces with weights
+// end, each segment preceded by a few empty positions that stand for the cost
+// of starting it; a persistent grid of P workgroups takes equal contiguous runs
+// of that list (stream-K).  A run that covers a whole single-segment unit
+// writes the bf16 output directly; any other piece (segment sigma, workgroup w)
+// writes its partial output, already divided by its row sums, and
+// natural-log lse to workspace slot sigma + w.  Pieces are ordered in both
+// sigma and w, so that slot is unique, and there are at most (#segments + P)
+// of them.  The merge kernel combines each row's pieces with weights
 // exp(lse - max lse).  This replaces a fixed segment count, which on a batch
 // of uneven lengths leaves a nearly empty second round of workgroups
 // (Modifications: segments chosen from CU parallelism and per-segment work).
@@ -22,11 +23,17 @@
 
 namespace pga {
 
-constexpr int kMinTilesPerWg = 4;  // shortest run a workgroup takes (256 keys)
+constexpr int kMinTilesPerWg = 4;  // shortest run a workgroup takes (in plan units)
+// Plan units charged for starting a piece of work: a workgroup that begins a
+// second piece reloads its queries, refills its pipeline and writes a partial
+// result, which costs about as much as streaming this many tiles.  Each
+// segment is preceded by this many units without keys in the flattened list.
+constexpr int kSegStartCost = 3;
 
-// Per-sequence work of the plan: 64-key tiles per kv head and segments per kv head.
+// Per-sequence work of the plan, per kv head: 64-key tiles, segments, and the
+// length in the flattened list (tiles plus the start cost of each segment).
 struct SeqWork {
-  int tiles, segs;
+  int tiles, segs, span;
 };
 __device__ __forceinline__ SeqWork seq_work_of(const VerifyArgs& a, int lq, int lk) {
   lq = min(lq, a.max_q_len);
@@ -34,6 +41,7 @@ __device__ __forceinline__ SeqWork seq_work_of(const VerifyArgs& a, int lq, int 
   SeqWork s;
   s.tiles = (lq > 0 && lk > 0) ? (lk + 63) >> 6 : 0;
   s.segs = s.tiles > 0 ? (s.tiles + a.seg_tiles - 1) / a.seg_tiles : 0;
+  s.span = s.tiles + kSegStartCost * s.segs;
   return s;
 }
 // Uniform b: scalar loads.
@@ -42,7 +50,7 @@ __device__ __forceinline__ SeqWork seq_work(const VerifyArgs& a, int b) {
 }
 // Per-lane b (out of range gives no work).
 __device__ __forceinline__ SeqWork seq_work_lane(const VerifyArgs& a, int b) {
-  if (b >= a.num_seqs) return SeqWork{0, 0};
+  if (b >= a.num_seqs) return SeqWork{0, 0, 0};
   return seq_work_of(a, a.cu_q[b + 1] - a.cu_q[b], a.lens_k[b]);
 }
 
@@ -56,9 +64,10 @@ __device__ __forceinline__ int wave_incl_scan(int x) {
   return x;
 }
 
-// Plan of one call, identical in every workgroup of both kernels: total tiles,
-// tiles per workgroup, and the tile / segment prefix (per kv head) of sequence
-// `target_b`, or of the sequence holding tile `target_t` when target_b < 0.
+// Plan of one call, identical in every workgroup: the total length of the
+// flattened list, its length per workgroup, and the list / segment prefix (per
+// kv head) of sequence `target_b`, or of the sequence holding list position
+// `target_t` when target_b < 0.
 // Called by a whole wave.
 struct PlanPos {
   int total, tpw, b, tile_prefix, seg_prefix;
@@ -67,7 +76,7 @@ __device__ PlanPos plan_scan(const VerifyArgs& a, int num_wg, int target_t, int 
   const int lane = lane_id();
   const int hkv = a.kv.num_kv_heads;
   int tot = 0;
-  for (int c = 0; c < a.num_seqs; c += 64) tot += __shfl(wave_incl_scan(seq_work_lane(a, c + lane).tiles), 63);
+  for (int c = 0; c < a.num_seqs; c += 64) tot += __shfl(wave_incl_scan(seq_work_lane(a, c + lane).span), 63);
   PlanPos p;
   p.total = tot * hkv;
   p.tpw = max(kMinTilesPerWg, (p.total + num_wg - 1) / num_wg);
@@ -77,17 +86,17 @@ __device__ PlanPos plan_scan(const VerifyArgs& a, int num_wg, int target_t, int 
   for (int c = 0; c < a.num_seqs; c += 64) {
     const int b = c + lane;
     const SeqWork s = seq_work_lane(a, b);
-    const int it = wave_incl_scan(s.tiles), is = wave_incl_scan(s.segs);
+    const int it = wave_incl_scan(s.span), is = wave_incl_scan(s.segs);
     bool hit;
     if (target_b >= 0)
       hit = (b == target_b);
     else
-      hit = s.tiles > 0 && (ts + it - s.tiles) * hkv <= target_t && target_t < (ts + it) * hkv;
+      hit = s.span > 0 && (ts + it - s.span) * hkv <= target_t && target_t < (ts + it) * hkv;
     const uint64_t m = __builtin_amdgcn_ballot_w64(hit);
     if (m) {
       const int src = __builtin_ctzll(m);
       p.b = c + src;
-      p.tile_prefix = ts + __shfl(it - s.tiles, src);
+      p.tile_prefix = ts + __shfl(it - s.span, src);
       p.seg_prefix = ss + __shfl(is - s.segs, src);
       break;
     }
@@ -130,8 +139,8 @@ __global__ __launch_bounds__(256, (KV == kFP8) ? 2 : 1) void verify_kernel(Verif
   if (b < 0 || t0 >= total) return;
   const int t1 = min(t0 + tpw, total);
   SeqWork sw = seq_work(a, b);
-  int g = (t0 - tprefix * hkv) / sw.tiles;
-  int tu = tprefix * hkv + g * sw.tiles;  // first tile of unit (b, g) in the flattened list
+  int g = (t0 - tprefix * hkv) / sw.span;
+  int tu = tprefix * hkv + g * sw.span;   // start of unit (b, g) in the flattened list
   int su = sprefix * hkv + g * sw.segs;   // first segment of unit (b, g)
   const float c2 = a.c2_base * load_scale(a.q_ds) * load_scale(a.kv.k_ds);
   const float vds = load_scale(a.kv.v_ds);
@@ -139,14 +148,25 @@ __global__ __launch_bounds__(256, (KV == kFP8) ? 2 : 1) void verify_kernel(Verif
   if (wg == 0 && threadIdx.x == 0) a.ws_plan[2 * a.num_seqs * hkv] = tpw;
   int cur = t0;
   while (cur < t1) {
-    const int lt0 = cur - tu;
-    if (lt0 == 0 && threadIdx.x == 0) {  // this workgroup starts the unit: record where it lies
+    // Segment s of the unit occupies [s * S, s * S + kSegStartCost + its tiles)
+    // of the unit's span; the first kSegStartCost units hold no keys.
+    const int S = kSegStartCost + a.seg_tiles;
+    const int x = cur - tu;
+    const int s = min(x / S, sw.segs - 1);
+    const int seg_tiles = s == sw.segs - 1 ? sw.tiles - s * a.seg_tiles : a.seg_tiles;
+    const int xr = max(x, s * S + kSegStartCost);           // first key-holding position of the piece
+    const int xe = min(s * S + kSegStartCost + seg_tiles, t1 - tu);
+    if (xe <= xr) {  // the run ends before the segment's first tile
+      cur = tu + xe;
+      continue;
+    }
+    const int lt0 = s * a.seg_tiles + (xr - s * S - kSegStartCost);
+    const int lt1 = s * a.seg_tiles + (xe - s * S - kSegStartCost);
+    const int lts1 = s * a.seg_tiles + seg_tiles;
+    if (lt0 == 0 && threadIdx.x == 0) {  // this workgroup holds the unit's first tile: record where it lies
       a.ws_plan[2 * (b * hkv + g)] = tu;
       a.ws_plan[2 * (b * hkv + g) + 1] = su;
     }
-    const int s = lt0 / a.seg_tiles;
-    const int lts1 = min((s + 1) * a.seg_tiles, sw.tiles);
-    const int lt1 = min(lts1, t1 - tu);
     const int tok0 = scalar_load(a.cu_q + b);
     const int lq = min(scalar_load(a.cu_q + b + 1) - tok0, a.max_q_len);
     const int lk = min(scalar_load(a.lens_k + b), a.max_kv_len);
@@ -199,9 +219,9 @@ __global__ __launch_bounds__(256, (KV == kFP8) ? 2 : 1) void verify_kernel(Verif
         }
       }
     }
-    cur = tu + lt1;
-    if (lt1 == sw.tiles) {  // next unit: next kv head, or the next sequence with work
-      tu += sw.tiles;
+    cur = tu + xe;
+    if (xe == sw.span) {  // next unit: next kv head, or the next sequence with work
+      tu += sw.span;
       su += sw.segs;
       if (++g == hkv) {
         g = 0;
@@ -249,7 +269,9 @@ __global__ __launch_bounds__(256) void verify_merge_kernel(VerifyArgs a) {
   const int tu = scalar_load(a.ws_plan + 2 * u);
   const int su = scalar_load(a.ws_plan + 2 * u + 1);
   const int tpw = scalar_load(a.ws_plan + 2 * a.num_seqs * hkv);
-  if (sw.segs == 1 && tu / tpw == (tu + sw.tiles - 1) / tpw) return;  // written directly
+  const int S = kSegStartCost + a.seg_tiles;
+  if (sw.segs == 1 && (tu + kSegStartCost) / tpw == (tu + kSegStartCost + sw.tiles - 1) / tpw)
+    return;  // written directly
   // Pieces per segment: lane s takes segment s (up to 64 segments at once),
   // so piece j's segment is found by comparisons against a prefix sum instead
   // of a division per segment per piece.
@@ -259,8 +281,9 @@ __global__ __launch_bounds__(256) void verify_merge_kernel(VerifyArgs a) {
     const int sl = s0 + lane;
     int first = 0, cnt = 0;
     if (sl < sw.segs) {
-      first = (tu + sl * a.seg_tiles) / tpw;
-      cnt = (tu + min((sl + 1) * a.seg_tiles, sw.tiles) - 1) / tpw - first + 1;
+      const int x0 = tu + sl * S + kSegStartCost;  // first tile of segment sl in the flattened list
+      first = x0 / tpw;
+      cnt = (x0 + min(a.seg_tiles, sw.tiles - sl * a.seg_tiles) - 1) / tpw - first + 1;
     }
     const int incl = wave_incl_scan(cnt);
     const int excl = incl - cnt;
