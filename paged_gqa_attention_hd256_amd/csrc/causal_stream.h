@@ -53,7 +53,8 @@ __device__ __forceinline__ T scalar_load(const T* p) {
 }
 
 // Stream keys [k_lo, k_hi) of kv head g of the sequence whose block-table row
-// is bt_row through LDS, calling tile.front(kt, tb) and then tile.back(vt, tb)
+// is bt_row through LDS (`first`: first_pages() of the same range), calling
+// tile.front(kt, tb) and then tile.back(vt, tb)
 // on every 64-key tile in every wave (kt / vt: the tile's K and V in LDS; tb:
 // its first key).  front may read only K and back only V and the exchange
 // area; a barrier separates them.  Every wave of the workgroup must call this.
@@ -62,9 +63,18 @@ __device__ __forceinline__ T scalar_load(const T* p) {
 // as front(i) is done with K of tile i (about 1.5 tiles ahead), V of tile i + 1
 // as soon as back(i - 1) is done with V of tile i - 1 (one tile ahead), so two
 // barriers per tile suffice and more of the gather is in flight.
+// Page ids of this wave's rows of the first two tiles of [k_lo, k_hi) (see
+// stream_keys).  Reading them before the queries load lets both reads overlap.
+__device__ __forceinline__ int2 first_pages(const KvArgs& kv, const int32_t* bt_row, int k_lo, int k_hi) {
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int p0 = __builtin_amdgcn_readfirstlane(min(k_lo + 16 * w, k_hi - 1) >> kv.page_shift);
+  const int p1 = __builtin_amdgcn_readfirstlane(min(k_lo + 64 + 16 * w, k_hi - 1) >> kv.page_shift);
+  return int2{k_hi > k_lo ? scalar_load(bt_row + p0) : 0, k_hi > k_lo + 64 ? scalar_load(bt_row + p1) : 0};
+}
+
 template <int KV, class Tile>
 __device__ __forceinline__ void stream_keys(CausalSmem<KV>& sm, const KvArgs& kv, const int32_t* bt_row, int g,
-                                            int k_lo, int k_hi, const Tile& tile) {
+                                            int k_lo, int k_hi, int2 first, const Tile& tile) {
   using G = TileGeom<KV>;
   constexpr int kRowsPerDma = 1024 / G::kRowBytes;  // rows one 1 KB DMA instruction fills
   constexpr int kDma = 16 / kRowsPerDma;            // per wave, for its 16 rows of K (or V)
@@ -102,10 +112,10 @@ __device__ __forceinline__ void stream_keys(CausalSmem<KV>& sm, const KvArgs& kv
   auto issue_v = [&](int it, int page) { issue(it, page, kv.v, kv.v_sh, kv.v_sp, kv.v_st, &sm.buf[it & 1][1][0]); };
 
   if (ntiles <= 0) return;
-  const int pg0 = page_of(0);
+  const int pg0 = first.x;
   issue_k(0, pg0);
   issue_v(0, pg0);
-  int pg1 = ntiles > 1 ? page_of(1) : 0;  // page of tile it + 1
+  int pg1 = first.y;  // page of tile it + 1
   if (ntiles > 1) {
     issue_k(1, pg1);
     issue_v(1, pg1);

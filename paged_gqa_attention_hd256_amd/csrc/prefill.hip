@@ -35,6 +35,8 @@ __global__ __launch_bounds__(256, (KV == kFP8) ? 2 : 1) void prefill_kernel(Pref
   const int tq = row_ok ? rho / a.r : 0;
   const int head = g * a.r + (row_ok ? rho - tq * a.r : 0);
   const int64_t tok = tok0 + t_lo + tq;
+  const int32_t* bt_row = a.kv.bt + (int64_t)b * a.kv.bt_stride;
+  const int2 first = first_pages(a.kv, bt_row, 0, k_hi);
   QFragT<KV> qf;
   load_q<QDT, KV>(qf, a.q, tok, a.hq, head, row_ok);
   const float c2 = a.c2_base * load_scale(a.q_ds) * load_scale(a.kv.k_ds);
@@ -46,7 +48,7 @@ __global__ __launch_bounds__(256, (KV == kFP8) ? 2 : 1) void prefill_kernel(Pref
   f32x4 o[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  stream_keys(sm, a.kv, a.kv.bt + (int64_t)b * a.kv.bt_stride, g, 0, k_hi,
+  stream_keys(sm, a.kv, bt_row, g, 0, k_hi, first,
               SplitTile<QDT, KV>{qf, c2 * qf.rscale, klim, min_lim, live, rs, o, sm.x});
   const float lrow = finish_rows(rs, live, sm.x);
   if (row_ok && (lane >> 4) == 0 && a.lse)

@@ -177,9 +177,11 @@ __global__ __launch_bounds__(256, (KV == kFP8) ? 2 : 1) void verify_kernel(Verif
     const int head = g * a.r + (row_ok ? rho - t * a.r : 0);
     const int64_t tok = tok0 + t;
     const bool live = 16 * w < rows;
+    const int k_lo = lt0 * 64, k_hi = min(lt1 * 64, lk);
+    const int32_t* bt_row = a.kv.bt + (int64_t)b * a.kv.bt_stride;
+    const int2 first = first_pages(a.kv, bt_row, k_lo, k_hi);
     QFragT<KV> qf;
     load_q<kBF16, KV>(qf, a.q, tok, a.hq, head, row_ok);
-    const int k_lo = lt0 * 64, k_hi = min(lt1 * 64, lk);
     const int klim = row_ok ? min(lk - lq + t, k_hi - 1) : -1;
     const int min_lim = min(lk - lq, k_hi - 1);
     RowStat rs;
@@ -187,7 +189,7 @@ __global__ __launch_bounds__(256, (KV == kFP8) ? 2 : 1) void verify_kernel(Verif
     f32x4 o[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-    stream_keys(sm, a.kv, a.kv.bt + (int64_t)b * a.kv.bt_stride, g, k_lo, k_hi,
+    stream_keys(sm, a.kv, bt_row, g, k_lo, k_hi, first,
                 SplitTile<kBF16, KV>{qf, c2 * qf.rscale, klim, min_lim, live, rs, o, sm.x});
     const float lrow = finish_rows(rs, live, sm.x);
     // A run that covers a whole uncut unit writes the output; any other piece
