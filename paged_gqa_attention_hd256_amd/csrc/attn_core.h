@@ -196,10 +196,35 @@ __device__ __forceinline__ void tile_softmax(WaveState& st, f32x4 (&s)[NMB], flo
   st.l += sum;
 }
 
-// O^T += V^T * P^T over the tile's 16 * NMB keys (32-key MFMA steps).
+// O^T += V^T * P^T over the tile's 16 * NMB keys (32-key MFMA steps; a
+// 16-key BF16 tile takes one 16-key step).
 template <int KV, int NMB>
 __device__ __forceinline__ void tile_pv(WaveState& st, const lds_t* vt, const f32x4 (&p)[NMB]) {
-  static_assert(NMB % 2 == 0, "tiles hold a multiple of 32 keys");
+  if constexpr (KV == kBF16 && NMB == 1) {
+    // P^T as the B operand: lane holds keys 4 (lane / 16) + j of its row, as
+    // the scores lie.  V^T: transpose-read source lane sl = 4e + q points at
+    // key 4 (lane / 16) + e, columns 4q .. 4q + 3 of the d-block.
+    using G = TileGeom<KV>;
+    const int lane = lane_id();
+    const int gq = lane >> 4, sl = lane & 15;
+    const int e = sl >> 2, q = sl & 3;
+    i16x4 ph, pl;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float x = p[0][j];
+      const __bf16 h = (__bf16)x;
+      ph[j] = __builtin_bit_cast(short, h);
+      pl[j] = __builtin_bit_cast(short, (__bf16)(x - (float)h));
+    }
+#pragma unroll
+    for (int mb = 0; mb < 16; ++mb) {
+      const i16x4 a = __builtin_bit_cast(i16x4, lds_tr16(vt + G::off(4 * gq + e, 2 * mb + (q >> 1)) + 8 * (q & 1)));
+      st.o[mb] = mfma_bf16_k16(a, ph, st.o[mb]);
+      st.o[mb] = mfma_bf16_k16(a, pl, st.o[mb]);
+    }
+    return;
+  }
+  static_assert(NMB % 2 == 0 || (KV == kBF16 && NMB == 1), "tiles hold a multiple of 32 keys");
   using G = TileGeom<KV>;
   const int lane = lane_id();
   const int gq = lane >> 4, sl = lane & 15;

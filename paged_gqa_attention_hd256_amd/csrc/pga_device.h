@@ -126,6 +126,11 @@ __device__ __forceinline__ f16x8 fp8x8_to_f16(i32x2 w) {
 __device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
+// 16x16x16 bf16: A lane l holds A[l % 16][4 * (l / 16) + j], B lane l holds
+// B[4 * (l / 16) + j][l % 16], j = 0..3 (bf16 bit patterns in shorts).
+__device__ __forceinline__ f32x4 mfma_bf16_k16(i16x4 a, i16x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
 __device__ __forceinline__ f32x4 mfma_f16(f16x8 a, f16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }

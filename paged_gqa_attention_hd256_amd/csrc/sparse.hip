@@ -24,8 +24,11 @@ constexpr int kSparseTableEntries = 1024;  // index-list chunk held in LDS per w
 template <int KV>
 struct SparseCfg {
   using G = TileGeom<KV>;
-  static constexpr int kWaves = (KV == kFP8) ? 4 : 2;
-  static constexpr int kTileKeys = 32;
+  // Four independent waves per CU: 32-key tiles of FP8 K and V, 16-key tiles
+  // of BF16 (two stages of K and V plus the index table fit 4 x 36 KB of LDS).
+  static constexpr int kWaves = 4;
+  static constexpr int kTileKeys = (KV == kFP8) ? 32 : 16;
+  static constexpr int kBlocks = kTileKeys / 16;  // 16-key MFMA blocks per tile
   static constexpr int kTileBytes = G::template tile_bytes<kTileKeys>();         // K or V of one tile
   static constexpr int kWaveBytes = 4 * kTileBytes + 4 * kSparseTableEntries;    // 2 buffers x (K, V) + table
   static constexpr int kRowsPerDma = 1024 / G::kRowBytes;
@@ -124,18 +127,19 @@ __global__ __launch_bounds__(SparseCfg<KV>::kWaves * 64) void sparse_kernel(Spar
       }
       const lds_t* kt = tiles + (2 * (it & 1) + 0) * C::kTileBytes;
       const lds_t* vt = tiles + (2 * (it & 1) + 1) * C::kTileBytes;
-      f32x4 sc[2];
-      tile_scores<KV, 2, true>(kt, qf, sc);
+      f32x4 sc[C::kBlocks];
+      tile_scores<KV, C::kBlocks, true>(kt, qf, sc);
       const lds_t* tt = table + 4 * (it * C::kTileKeys);
       const i32x4 v0 = lds_load<i32x4>(tt + 4 * (4 * gq));
-      const i32x4 v1 = lds_load<i32x4>(tt + 4 * (16 + 4 * gq));
+      i32x4 v1 = v0;
+      if constexpr (C::kBlocks == 2) v1 = lds_load<i32x4>(tt + 4 * (16 + 4 * gq));
       tile_softmax<true>(st, sc, c2, [&](int key) {
         const int q = key - 4 * gq;  // 0..3 in block 0, 16..19 in block 1
         const int e = q & 3;
         const int v = (q < 16) ? v0[e] : v1[e];
         return v >= 0;
       });
-      tile_pv<KV, 2>(st, vt, sc);
+      tile_pv<KV, C::kBlocks>(st, vt, sc);
     }
   }
 
