@@ -92,8 +92,8 @@ typedef struct pga_paged_kv {
   int32_t page_size;          /* tokens per page: a power of two, 16..1024 */
   int32_t num_pages;          /* pages in the pool; entries outside [0, num_pages) are never read */
   int32_t reserved;           /* set to 0 */
-  int64_t k_stride_page, k_stride_token, k_stride_head;
-  int64_t v_stride_page, v_stride_token, v_stride_head;
+  int64_t k_stride_page, k_stride_token, k_stride_head;  /* elements; multiples of 16 bytes; */
+  int64_t v_stride_page, v_stride_token, v_stride_head;  /* page_size * stride_token < 2 GiB */
   const int32_t* block_table; /* [num_seqs, block_table_stride] physical page ids */
   int64_t block_table_stride; /* >= ceil(max KV length / page_size) */
   const float* k_descale;     /* device scalar or NULL (1.0) */

@@ -51,6 +51,9 @@ int check_kv(const pga_paged_kv* kv, int32_t num_q_heads, int64_t pages_per_seq)
                          kv->v_stride_page, kv->v_stride_token, kv->v_stride_head};
   for (int64_t s : st)
     if (s < 0 || s % per16 != 0) return PGA_ERR_UNSUPPORTED;
+  // Within a page, token rows are addressed by 32-bit byte offsets.
+  const int64_t tok_bytes = std::max(kv->k_stride_token, kv->v_stride_token) * elt_bytes(kv->dtype);
+  if (tok_bytes * kv->page_size + kHeadDim * elt_bytes(kv->dtype) > INT32_MAX) return PGA_ERR_UNSUPPORTED;
   if (!aligned(kv->k_cache, 16) || !aligned(kv->v_cache, 16)) return PGA_ERR_UNSUPPORTED;
   if (kv->block_table_stride < 0 || (pages_per_seq > 0 && kv->block_table_stride < pages_per_seq))
     return PGA_ERR_SHAPE;

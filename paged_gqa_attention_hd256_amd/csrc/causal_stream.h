@@ -91,25 +91,34 @@ __device__ __forceinline__ void stream_keys(CausalSmem<KV>& sm, const KvArgs& kv
     const int pidx = __builtin_amdgcn_readfirstlane(min(key0, k_hi - 1) >> kv.page_shift);
     return scalar_load(bt_row + pidx);
   };
-  // kDma DMA instructions per call, whatever the keys (absent keys read zeros).
-  auto issue = [&](int it, int page, const uint8_t* base, int64_t sh, int64_t sp, int64_t st, char* dst) {
+  // kDma DMA instructions per call, from the wave's page (a uniform base) plus
+  // a 32-bit offset per lane.  Keys at or past k_hi read key k_hi - 1 instead
+  // (finite data that the mask gives probability 0); a page id outside the
+  // pool reads zeros.
+  // LDS byte address of the tile buffers (a constant: sm is a static LDS object).
+  const unsigned lds_buf = (unsigned)(uintptr_t)(lds_t*)&sm.buf[0][0][0];
+  auto issue = [&](int it, int page, const uint8_t* base, int64_t sh, int64_t sp, int64_t st, unsigned dst) {
     const int tb = k_lo + it * 64;
     const bool page_ok = page >= 0 && page < kv.num_pages;
-    const uint8_t* pbase = base + g * sh + (int64_t)page * sp;
+    const uint64_t pbase = page_ok ? (uint64_t)(uintptr_t)(base + g * sh + (int64_t)page * sp)
+                                   : (uint64_t)(uintptr_t)g_zero16;
 #pragma unroll
     for (int u = 0; u < kDma; ++u) {
       const int row0 = 16 * w + u * kRowsPerDma;
       const int row = row0 + lane / G::kChunks;
       const int chunk = (lane % G::kChunks) ^ (row & (G::kChunks - 1));
-      const int key = tb + row;
-      const bool ok = page_ok && key < k_hi;
-      const uint8_t* src = ok ? pbase + (key & (kv.page_size - 1)) * st + chunk * 16
-                              : reinterpret_cast<const uint8_t*>(g_zero16);
-      dma16(src, (lds_t*)(dst + row0 * G::kRowBytes));
+      const unsigned key = (unsigned)min(tb + row, k_hi - 1);
+      const unsigned off = page_ok ? (key & (kv.page_size - 1)) * (unsigned)st + chunk * 16 : 0u;
+      dma16_off(pbase, off, dst + row0 * G::kRowBytes);
     }
   };
-  auto issue_k = [&](int it, int page) { issue(it, page, kv.k, kv.k_sh, kv.k_sp, kv.k_st, &sm.buf[it & 1][0][0]); };
-  auto issue_v = [&](int it, int page) { issue(it, page, kv.v, kv.v_sh, kv.v_sp, kv.v_st, &sm.buf[it & 1][1][0]); };
+  constexpr unsigned kTile = CausalSmem<KV>::kTileBytes;
+  auto issue_k = [&](int it, int page) {
+    issue(it, page, kv.k, kv.k_sh, kv.k_sp, kv.k_st, lds_buf + (2 * (it & 1) + 0) * kTile);
+  };
+  auto issue_v = [&](int it, int page) {
+    issue(it, page, kv.v, kv.v_sh, kv.v_sp, kv.v_st, lds_buf + (2 * (it & 1) + 1) * kTile);
+  };
 
   if (ntiles <= 0) return;
   const int pg0 = first.x;
