@@ -37,13 +37,10 @@ struct CausalSmem {
   Exchange<KV> x;
 };
 
-// Running maximum (log2 domain) and this lane's partial row sum of one softmax row.
+// Running maximum (log2 domain) of one softmax row.
 struct RowStat {
-  float m, l;
-  __device__ __forceinline__ void init() {
-    m = kNegInf;
-    l = 0.f;
-  }
+  float m;
+  __device__ __forceinline__ void init() { m = kNegInf; }
 };
 
 // Uniform load through the scalar data cache (read-only data, uniform address).
@@ -92,32 +89,53 @@ __device__ __forceinline__ void stream_keys(CausalSmem<KV>& sm, const KvArgs& kv
     return scalar_load(bt_row + pidx);
   };
   // kDma DMA instructions per call, from the wave's page (a uniform base) plus
-  // a 32-bit offset per lane.  Keys at or past k_hi read key k_hi - 1 instead
-  // (finite data that the mask gives probability 0); a page id outside the
+  // a 32-bit offset per lane.  Tiles start at multiples of 64 keys, so a row's
+  // slot in its page is (tb mod page_size) + (row mod page_size): the lane
+  // part is fixed for the whole stream and the rest joins the uniform base.
+  // In the range's last tile, keys at or past k_hi read key k_hi - 1 instead
+  // (finite data that the mask gives probability 0).  A page id outside the
   // pool reads zeros.
+  const unsigned pmask = kv.page_size - 1;
+  unsigned lane_k[kDma], lane_v[kDma];
+#pragma unroll
+  for (int u = 0; u < kDma; ++u) {
+    const int row = 16 * w + u * kRowsPerDma + lane / G::kChunks;
+    const unsigned chunk = (lane % G::kChunks) ^ (row & (G::kChunks - 1));
+    lane_k[u] = (row & pmask) * (unsigned)kv.k_st + chunk * 16;
+    lane_v[u] = (row & pmask) * (unsigned)kv.v_st + chunk * 16;
+  }
   // LDS byte address of the tile buffers (a constant: sm is a static LDS object).
   const unsigned lds_buf = (unsigned)(uintptr_t)(lds_t*)&sm.buf[0][0][0];
-  auto issue = [&](int it, int page, const uint8_t* base, int64_t sh, int64_t sp, int64_t st, unsigned dst) {
+  auto issue = [&](int it, int page, const uint8_t* base, int64_t sh, int64_t sp, int64_t st,
+                   const unsigned (&lane_off)[kDma], unsigned dst) {
     const int tb = k_lo + it * 64;
     const bool page_ok = page >= 0 && page < kv.num_pages;
     const uint64_t pbase = page_ok ? (uint64_t)(uintptr_t)(base + g * sh + (int64_t)page * sp)
                                    : (uint64_t)(uintptr_t)g_zero16;
+    if (!page_ok) {
 #pragma unroll
-    for (int u = 0; u < kDma; ++u) {
-      const int row0 = 16 * w + u * kRowsPerDma;
-      const int row = row0 + lane / G::kChunks;
-      const int chunk = (lane % G::kChunks) ^ (row & (G::kChunks - 1));
-      const unsigned key = (unsigned)min(tb + row, k_hi - 1);
-      const unsigned off = page_ok ? (key & (kv.page_size - 1)) * (unsigned)st + chunk * 16 : 0u;
-      dma16_off(pbase, off, dst + row0 * G::kRowBytes);
+      for (int u = 0; u < kDma; ++u) dma16_off(pbase, 0u, dst + (16 * w + u * kRowsPerDma) * G::kRowBytes);
+    } else if (tb + 64 <= k_hi) {  // every key of the tile exists
+      const uint64_t tbase = pbase + (uint64_t)((tb & pmask) * (unsigned)st);
+#pragma unroll
+      for (int u = 0; u < kDma; ++u) dma16_off(tbase, lane_off[u], dst + (16 * w + u * kRowsPerDma) * G::kRowBytes);
+    } else {
+#pragma unroll
+      for (int u = 0; u < kDma; ++u) {
+        const int row0 = 16 * w + u * kRowsPerDma;
+        const int row = row0 + lane / G::kChunks;
+        const unsigned chunk = (lane % G::kChunks) ^ (row & (G::kChunks - 1));
+        const unsigned key = (unsigned)min(tb + row, k_hi - 1);
+        dma16_off(pbase, (key & pmask) * (unsigned)st + chunk * 16, dst + row0 * G::kRowBytes);
+      }
     }
   };
   constexpr unsigned kTile = CausalSmem<KV>::kTileBytes;
   auto issue_k = [&](int it, int page) {
-    issue(it, page, kv.k, kv.k_sh, kv.k_sp, kv.k_st, lds_buf + (2 * (it & 1) + 0) * kTile);
+    issue(it, page, kv.k, kv.k_sh, kv.k_sp, kv.k_st, lane_k, lds_buf + (2 * (it & 1) + 0) * kTile);
   };
   auto issue_v = [&](int it, int page) {
-    issue(it, page, kv.v, kv.v_sh, kv.v_sp, kv.v_st, lds_buf + (2 * (it & 1) + 1) * kTile);
+    issue(it, page, kv.v, kv.v_sh, kv.v_sp, kv.v_st, lane_v, lds_buf + (2 * (it & 1) + 1) * kTile);
   };
 
   if (ntiles <= 0) return;
@@ -150,8 +168,8 @@ __device__ __forceinline__ void stream_keys(CausalSmem<KV>& sm, const KvArgs& kv
 
 // Softmax of this wave's 16 rows on a tile (scores s from tile_scores), as
 // tile_softmax does it, except that the rescale factor is published for the PV
-// waves instead of being applied, and the probabilities go to LDS as PV
-// operands.
+// waves instead of being applied, the probabilities go to LDS as PV operands,
+// and the row sums are left to the PV step (see pv_quarter).
 template <int KV, bool MASKED, class Vis>
 __device__ __forceinline__ void softmax_publish(RowStat& rs, f32x4 (&s)[4], float c2, Vis visible,
                                                 Exchange<KV>& x, int w) {
@@ -174,21 +192,13 @@ __device__ __forceinline__ void softmax_publish(RowStat& rs, f32x4 (&s)[4], floa
   if (grow != 0) {  // wave-uniform
     const float m_new = fmaxf(rs.m, mt);
     alpha = m_new == rs.m ? 1.f : fast_exp2(rs.m - m_new);
-    rs.l *= alpha;
     rs.m = m_new;
   }
   const float m_use = (rs.m == kNegInf) ? 0.f : rs.m;
-  float sum = 0.f;
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb) {
+  for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float p = fast_exp2(s[mb][i] - m_use);
-      s[mb][i] = p;
-      sum += p;
-    }
-  }
-  rs.l += sum;
+    for (int i = 0; i < 4; ++i) s[mb][i] = fast_exp2(s[mb][i] - m_use);
   if (gq == 0) x.row[16 * w + n] = alpha;
   if (lane == 0) x.grow[w] = grow != 0;
   // B operand of the 32-key step t: keys 32t + 4gq + i and 32t + 16 + 4gq + i.
@@ -229,8 +239,13 @@ __device__ __forceinline__ void publish_nothing(Exchange<KV>& x, int w) {
 // O^T += V^T P^T for head dimensions 64w .. 64w + 63 of all 64 rows, after
 // applying the published rescale factors: o[4 * rb + db] holds rows
 // 16rb + lane % 16 and dims 64w + 16db + 4 (lane / 16) + i.
+//
+// The row sums of the wave's own softmax rows (row block w) come from the same
+// MFMAs with an all-ones A operand: lsum[i] = sum of this tile's P of row
+// 16w + lane % 16 (as rounded for PV), accumulated and rescaled like O.
 template <int KV>
-__device__ __forceinline__ void pv_quarter(f32x4 (&o)[16], const lds_t* vt, const Exchange<KV>& x, int w) {
+__device__ __forceinline__ void pv_quarter(f32x4 (&o)[16], f32x4& lsum, const lds_t* vt, const Exchange<KV>& x,
+                                           int w) {
   using G = TileGeom<KV>;
   const int lane = lane_id();
   const int gq = lane >> 4, sl = lane & 15;
@@ -242,6 +257,7 @@ __device__ __forceinline__ void pv_quarter(f32x4 (&o)[16], const lds_t* vt, cons
 #pragma unroll
       for (int db = 0; db < 4; ++db) o[4 * rb + db] *= al;
     }
+    lsum *= x.row[16 * w + sl];
   }
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
@@ -258,6 +274,9 @@ __device__ __forceinline__ void pv_quarter(f32x4 (&o)[16], const lds_t* vt, cons
 #pragma unroll
         for (int rb = 0; rb < 4; ++rb) o[4 * rb + db] = mfma_f16(a, pb[rb], o[4 * rb + db]);
       }
+      constexpr f16x8 ones = {(_Float16)1.f, (_Float16)1.f, (_Float16)1.f, (_Float16)1.f,
+                              (_Float16)1.f, (_Float16)1.f, (_Float16)1.f, (_Float16)1.f};
+      lsum = mfma_f16(ones, __builtin_bit_cast(f16x8, x.p[w][t][0][lane]), lsum);
     } else {
       bf16x8 ph[4], pl[4];
 #pragma unroll
@@ -280,6 +299,10 @@ __device__ __forceinline__ void pv_quarter(f32x4 (&o)[16], const lds_t* vt, cons
           o[4 * rb + db] = mfma_bf16(a, pl[rb], o[4 * rb + db]);
         }
       }
+      const bf16x8 ones = {(__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f,
+                           (__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f};
+      lsum = mfma_bf16(ones, __builtin_bit_cast(bf16x8, x.p[w][t][0][lane]), lsum);
+      lsum = mfma_bf16(ones, __builtin_bit_cast(bf16x8, x.p[w][t][1][lane]), lsum);
     }
   }
 }
@@ -297,6 +320,7 @@ struct SplitTile {
   bool live;
   RowStat& rs;
   f32x4 (&o)[16];
+  f32x4& lsum;
   Exchange<KV>& x;
   __device__ __forceinline__ void front(const lds_t* kt, int tb) const {
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -313,18 +337,18 @@ struct SplitTile {
     }
   }
   __device__ __forceinline__ void back(const lds_t* vt, int) const {
-    pv_quarter<KV>(o, vt, x, __builtin_amdgcn_readfirstlane(threadIdx.x >> 6));
+    pv_quarter<KV>(o, lsum, vt, x, __builtin_amdgcn_readfirstlane(threadIdx.x >> 6));
   }
 };
 
-// After the last tile: each softmax wave publishes its rows' sums (0 for a wave
-// without live rows) so that every wave can normalise its PV quarter; returns
-// this lane's row sum.  Contains a barrier.
+// After the last tile: each wave publishes the sums of its softmax rows (0 for
+// a wave without live rows) so that every wave can normalise its PV quarter;
+// returns this lane's row sum.  Contains a barrier.
 template <int KV>
-__device__ __forceinline__ float finish_rows(const RowStat& rs, bool live, Exchange<KV>& x) {
+__device__ __forceinline__ float finish_rows(const f32x4& lsum, bool live, Exchange<KV>& x) {
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = lane_id();
-  const float lrow = live ? group4_sum(rs.l) : 0.f;
+  const float lrow = live ? lsum[0] : 0.f;
   if (lane < 16) x.row[16 * w + lane] = lrow;
   barrier_publish();
   return lrow;

@@ -48,9 +48,10 @@ __global__ __launch_bounds__(256, (KV == kFP8) ? 2 : 1) void prefill_kernel(Pref
   f32x4 o[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  f32x4 lsum = {0.f, 0.f, 0.f, 0.f};
   stream_keys(sm, a.kv, bt_row, g, 0, k_hi, first,
-              SplitTile<QDT, KV>{qf, c2 * qf.rscale, klim, min_lim, live, rs, o, sm.x});
-  const float lrow = finish_rows(rs, live, sm.x);
+              SplitTile<QDT, KV>{qf, c2 * qf.rscale, klim, min_lim, live, rs, o, lsum, sm.x});
+  const float lrow = finish_rows(lsum, live, sm.x);
   if (row_ok && (lane >> 4) == 0 && a.lse)
     a.lse[tok * a.hq + head] = lrow > 0.f ? (rs.m + log2f(lrow)) * kLn2 : kNegInf;
   const float vds = load_scale(a.kv.v_ds);

@@ -189,9 +189,10 @@ __global__ __launch_bounds__(256, (KV == kFP8) ? 2 : 1) void verify_kernel(Verif
     f32x4 o[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    f32x4 lsum = {0.f, 0.f, 0.f, 0.f};
     stream_keys(sm, a.kv, bt_row, g, k_lo, k_hi, first,
-                SplitTile<kBF16, KV>{qf, c2 * qf.rscale, klim, min_lim, live, rs, o, sm.x});
-    const float lrow = finish_rows(rs, live, sm.x);
+                SplitTile<kBF16, KV>{qf, c2 * qf.rscale, klim, min_lim, live, rs, o, lsum, sm.x});
+    const float lrow = finish_rows(lsum, live, sm.x);
     // A run that covers a whole uncut unit writes the output; any other piece
     // writes its normalised fp32 rows and their lse to its workspace slot.
     const bool direct = lt0 == s * a.seg_tiles && lt1 == lts1 && sw.segs == 1;
