@@ -1,19 +1,19 @@
 // Streaming of a contiguous key range of one (sequence, kv head) through LDS,
 // shared by the verify and prefill kernels, and the attention of the
-// workgroup's 64 query rows on each streamed tile.
+// workgroup's 16 * NW query rows on each streamed tile (NW = 4 or 8 waves).
 //
-// A workgroup of four waves walks keys [k_lo, k_hi) in 64-key tiles.  Each
-// wave fetches 16 rows of every tile (K and V) by 16-byte global->LDS DMA into
-// a double buffer.  The page of a wave's 16 rows is read with a scalar load, so
+// A workgroup of NW waves walks keys [k_lo, k_hi) in 64-key tiles.  Each wave
+// fetches 64 / NW rows of every tile (K and V) by 16-byte global->LDS DMA into
+// a double buffer.  The page of a wave's rows is read with a scalar load, so
 // the only vector-memory instructions in flight are the DMA and the wait for
 // tile i can let tile i + 1 stay in flight.
 //
 // On a tile the work is split two ways.  For QK^T and the softmax, wave w owns
-// query rows 16w .. 16w + 15 (its scores, running maximum and row sum); it
-// publishes the probabilities, already in the B-operand layout of the PV
-// MFMA, and its rows' rescale factors to LDS.  For PV, wave w owns head
-// dimensions 64w .. 64w + 63 of all 64 rows, so each wave reads and widens a
-// quarter of the V tile instead of all of it.
+// query rows 16w .. 16w + 15 (its scores and running maximum); it publishes
+// the probabilities, already in the B-operand layout of the PV MFMA, and its
+// rows' rescale factors to LDS.  For PV, wave w owns head dimensions
+// (256 / NW) w .. (256 / NW)(w + 1) - 1 of all rows, so each wave reads and
+// widens a 1/NW share of the V tile instead of all of it.
 #pragma once
 
 #include "attn_core.h"
@@ -22,19 +22,20 @@
 namespace pga {
 
 // Exchange area between the softmax of a tile and its PV product.
-template <int KV>
+template <int KV, int NW>
 struct Exchange {
   static constexpr int kPVec = (KV == kFP8) ? 1 : 2;  // 16-byte P fragments per lane: fp16, or bf16 high + low
-  i32x4 p[4][2][kPVec][64];                           // [row block][32-key step][part][lane]
-  float row[64];  // per row: rescale factor of the current tile; at the end, the row sum
-  int grow[4];    // per softmax wave: whether any of its rows was rescaled on this tile
+  i32x4 p[NW][2][kPVec][64];                          // [row block][32-key step][part][lane]
+  float row[16 * NW];  // per row: rescale factor of the current tile; at the end, the row sum
+  int grow[NW];        // per softmax wave: whether any of its rows was rescaled on this tile
 };
 
-template <int KV>
+template <int KV, int NW>
 struct CausalSmem {
+  static constexpr int kWaves = NW;
   static constexpr int kTileBytes = TileGeom<KV>::template tile_bytes<64>();
   char buf[2][2][kTileBytes];  // [buffer][K, V]
-  Exchange<KV> x;
+  Exchange<KV, NW> x;
 };
 
 // Running maximum (log2 domain) of one softmax row.
@@ -62,29 +63,31 @@ __device__ __forceinline__ T scalar_load(const T* p) {
 // barriers per tile suffice and more of the gather is in flight.
 // Page ids of this wave's rows of the first two tiles of [k_lo, k_hi) (see
 // stream_keys).  Reading them before the queries load lets both reads overlap.
+template <int NW>
 __device__ __forceinline__ int2 first_pages(const KvArgs& kv, const int32_t* bt_row, int k_lo, int k_hi) {
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int p0 = __builtin_amdgcn_readfirstlane(min(k_lo + 16 * w, k_hi - 1) >> kv.page_shift);
-  const int p1 = __builtin_amdgcn_readfirstlane(min(k_lo + 64 + 16 * w, k_hi - 1) >> kv.page_shift);
+  const int p0 = __builtin_amdgcn_readfirstlane(min(k_lo + (64 / NW) * w, k_hi - 1) >> kv.page_shift);
+  const int p1 = __builtin_amdgcn_readfirstlane(min(k_lo + 64 + (64 / NW) * w, k_hi - 1) >> kv.page_shift);
   return int2{k_hi > k_lo ? scalar_load(bt_row + p0) : 0, k_hi > k_lo + 64 ? scalar_load(bt_row + p1) : 0};
 }
 
-template <int KV, class Tile>
-__device__ __forceinline__ void stream_keys(CausalSmem<KV>& sm, const KvArgs& kv, const int32_t* bt_row, int g,
+template <int KV, int NW, class Tile>
+__device__ __forceinline__ void stream_keys(CausalSmem<KV, NW>& sm, const KvArgs& kv, const int32_t* bt_row, int g,
                                             int k_lo, int k_hi, int2 first, const Tile& tile) {
   using G = TileGeom<KV>;
-  constexpr int kRowsPerDma = 1024 / G::kRowBytes;  // rows one 1 KB DMA instruction fills
-  constexpr int kDma = 16 / kRowsPerDma;            // per wave, for its 16 rows of K (or V)
+  constexpr int kRowsPerWave = 64 / NW;                   // rows of a tile each wave fetches
+  constexpr int kRowsPerDma = 1024 / G::kRowBytes;        // rows one 1 KB DMA instruction fills
+  constexpr int kDma = kRowsPerWave / kRowsPerDma;        // per wave, for its rows of K (or V)
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = lane_id();
   const int ntiles = (k_hi - k_lo + 63) >> 6;
 
-  // This wave's rows of a tile (16w .. 16w + 15) lie in one page: pages hold
-  // at least 16 tokens and tiles start at multiples of 64.  Page ids are read
+  // This wave's rows of a tile lie in one page: pages hold at least 16 tokens
+  // and tiles start at multiples of 64.  Page ids are read
   // with scalar loads two tiles ahead, so the read (often a cache miss:
   // block-table rows are long) never delays a DMA issue.
   auto page_of = [&](int it) {
-    const int key0 = k_lo + it * 64 + 16 * w;
+    const int key0 = k_lo + it * 64 + kRowsPerWave * w;
     const int pidx = __builtin_amdgcn_readfirstlane(min(key0, k_hi - 1) >> kv.page_shift);
     return scalar_load(bt_row + pidx);
   };
@@ -99,7 +102,7 @@ __device__ __forceinline__ void stream_keys(CausalSmem<KV>& sm, const KvArgs& kv
   unsigned lane_k[kDma], lane_v[kDma];
 #pragma unroll
   for (int u = 0; u < kDma; ++u) {
-    const int row = 16 * w + u * kRowsPerDma + lane / G::kChunks;
+    const int row = kRowsPerWave * w + u * kRowsPerDma + lane / G::kChunks;
     const unsigned chunk = (lane % G::kChunks) ^ (row & (G::kChunks - 1));
     lane_k[u] = (row & pmask) * (unsigned)kv.k_st + chunk * 16;
     lane_v[u] = (row & pmask) * (unsigned)kv.v_st + chunk * 16;
@@ -114,15 +117,16 @@ __device__ __forceinline__ void stream_keys(CausalSmem<KV>& sm, const KvArgs& kv
                                    : (uint64_t)(uintptr_t)g_zero16;
     if (!page_ok) {
 #pragma unroll
-      for (int u = 0; u < kDma; ++u) dma16_off(pbase, 0u, dst + (16 * w + u * kRowsPerDma) * G::kRowBytes);
+      for (int u = 0; u < kDma; ++u) dma16_off(pbase, 0u, dst + (kRowsPerWave * w + u * kRowsPerDma) * G::kRowBytes);
     } else if (tb + 64 <= k_hi) {  // every key of the tile exists
       const uint64_t tbase = pbase + (uint64_t)((tb & pmask) * (unsigned)st);
 #pragma unroll
-      for (int u = 0; u < kDma; ++u) dma16_off(tbase, lane_off[u], dst + (16 * w + u * kRowsPerDma) * G::kRowBytes);
+      for (int u = 0; u < kDma; ++u)
+        dma16_off(tbase, lane_off[u], dst + (kRowsPerWave * w + u * kRowsPerDma) * G::kRowBytes);
     } else {
 #pragma unroll
       for (int u = 0; u < kDma; ++u) {
-        const int row0 = 16 * w + u * kRowsPerDma;
+        const int row0 = kRowsPerWave * w + u * kRowsPerDma;
         const int row = row0 + lane / G::kChunks;
         const unsigned chunk = (lane % G::kChunks) ^ (row & (G::kChunks - 1));
         const unsigned key = (unsigned)min(tb + row, k_hi - 1);
@@ -130,7 +134,7 @@ __device__ __forceinline__ void stream_keys(CausalSmem<KV>& sm, const KvArgs& kv
       }
     }
   };
-  constexpr unsigned kTile = CausalSmem<KV>::kTileBytes;
+  constexpr unsigned kTile = CausalSmem<KV, NW>::kTileBytes;
   auto issue_k = [&](int it, int page) {
     issue(it, page, kv.k, kv.k_sh, kv.k_sp, kv.k_st, lane_k, lds_buf + (2 * (it & 1) + 0) * kTile);
   };
@@ -170,9 +174,9 @@ __device__ __forceinline__ void stream_keys(CausalSmem<KV>& sm, const KvArgs& kv
 // tile_softmax does it, except that the rescale factor is published for the PV
 // waves instead of being applied, the probabilities go to LDS as PV operands,
 // and the row sums are left to the PV step (see pv_quarter).
-template <int KV, bool MASKED, class Vis>
+template <int KV, bool MASKED, class Vis, int NW>
 __device__ __forceinline__ void softmax_publish(RowStat& rs, f32x4 (&s)[4], float c2, Vis visible,
-                                                Exchange<KV>& x, int w) {
+                                                Exchange<KV, NW>& x, int w) {
   const int lane = lane_id();
   const int gq = lane >> 4, n = lane & 15;
   float mt = kNegInf;
@@ -225,78 +229,82 @@ __device__ __forceinline__ void softmax_publish(RowStat& rs, f32x4 (&s)[4], floa
 }
 
 // A wave without live query rows: zero probabilities and no rescale.
-template <int KV>
-__device__ __forceinline__ void publish_nothing(Exchange<KV>& x, int w) {
+template <int KV, int NW>
+__device__ __forceinline__ void publish_nothing(Exchange<KV, NW>& x, int w) {
   const int lane = lane_id();
   if (lane < 16) x.row[16 * w + lane] = 1.f;
   if (lane == 0) x.grow[w] = 0;
 #pragma unroll
   for (int t = 0; t < 2; ++t)
 #pragma unroll
-    for (int c = 0; c < Exchange<KV>::kPVec; ++c) x.p[w][t][c][lane] = i32x4{0, 0, 0, 0};
+    for (int c = 0; c < Exchange<KV, NW>::kPVec; ++c) x.p[w][t][c][lane] = i32x4{0, 0, 0, 0};
 }
 
-// O^T += V^T P^T for head dimensions 64w .. 64w + 63 of all 64 rows, after
-// applying the published rescale factors: o[4 * rb + db] holds rows
-// 16rb + lane % 16 and dims 64w + 16db + 4 (lane / 16) + i.
+// O^T += V^T P^T for head dimensions (256 / NW) w .. of all 16 NW rows, after
+// applying the published rescale factors: with DB = 16 / NW d-blocks per wave,
+// o[DB * rb + db] holds rows 16rb + lane % 16 and dims
+// (256 / NW) w + 16db + 4 (lane / 16) + i.
 //
 // The row sums of the wave's own softmax rows (row block w) come from the same
 // MFMAs with an all-ones A operand: lsum[i] = sum of this tile's P of row
 // 16w + lane % 16 (as rounded for PV), accumulated and rescaled like O.
-template <int KV>
-__device__ __forceinline__ void pv_quarter(f32x4 (&o)[16], f32x4& lsum, const lds_t* vt, const Exchange<KV>& x,
+template <int KV, int NW>
+__device__ __forceinline__ void pv_quarter(f32x4 (&o)[16], f32x4& lsum, const lds_t* vt, const Exchange<KV, NW>& x,
                                            int w) {
   using G = TileGeom<KV>;
+  constexpr int DB = 16 / NW;
   const int lane = lane_id();
   const int gq = lane >> 4, sl = lane & 15;
-  const int any = x.grow[0] | x.grow[1] | x.grow[2] | x.grow[3];
+  int any = 0;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) any |= x.grow[i];
   if (__builtin_amdgcn_readfirstlane(any) != 0) {
 #pragma unroll
-    for (int rb = 0; rb < 4; ++rb) {
+    for (int rb = 0; rb < NW; ++rb) {
       const float al = x.row[16 * rb + sl];
 #pragma unroll
-      for (int db = 0; db < 4; ++db) o[4 * rb + db] *= al;
+      for (int db = 0; db < DB; ++db) o[DB * rb + db] *= al;
     }
     lsum *= x.row[16 * w + sl];
   }
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
     if constexpr (KV == kFP8) {
-      f16x8 pb[4];
+      f16x8 pb[NW];
 #pragma unroll
-      for (int rb = 0; rb < 4; ++rb) pb[rb] = __builtin_bit_cast(f16x8, x.p[rb][t][0][lane]);
+      for (int rb = 0; rb < NW; ++rb) pb[rb] = __builtin_bit_cast(f16x8, x.p[rb][t][0][lane]);
       // transpose-read source: lane sl = 2e + q points at key(e), bytes 8q..8q+7 of the d-block
       const int e = sl >> 1, q = sl & 1;
       const int key = 32 * t + 16 * (e >> 2) + 4 * gq + (e & 3);
 #pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        const f16x8 a = fp8x8_to_f16(lds_tr8(vt + G::off(key, 4 * w + db) + 8 * q));
+      for (int db = 0; db < DB; ++db) {
+        const f16x8 a = fp8x8_to_f16(lds_tr8(vt + G::off(key, DB * w + db) + 8 * q));
 #pragma unroll
-        for (int rb = 0; rb < 4; ++rb) o[4 * rb + db] = mfma_f16(a, pb[rb], o[4 * rb + db]);
+        for (int rb = 0; rb < NW; ++rb) o[DB * rb + db] = mfma_f16(a, pb[rb], o[DB * rb + db]);
       }
       constexpr f16x8 ones = {(_Float16)1.f, (_Float16)1.f, (_Float16)1.f, (_Float16)1.f,
                               (_Float16)1.f, (_Float16)1.f, (_Float16)1.f, (_Float16)1.f};
       lsum = mfma_f16(ones, __builtin_bit_cast(f16x8, x.p[w][t][0][lane]), lsum);
     } else {
-      bf16x8 ph[4], pl[4];
+      bf16x8 ph[NW], pl[NW];
 #pragma unroll
-      for (int rb = 0; rb < 4; ++rb) {
+      for (int rb = 0; rb < NW; ++rb) {
         ph[rb] = __builtin_bit_cast(bf16x8, x.p[rb][t][0][lane]);
         pl[rb] = __builtin_bit_cast(bf16x8, x.p[rb][t][1][lane]);
       }
       // transpose-read source: lane sl = 4e + q points at key(e), columns 4q..4q+3
       const int e = sl >> 2, q = sl & 3;
 #pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        const int chunk = 2 * (4 * w + db) + (q >> 1);
+      for (int db = 0; db < DB; ++db) {
+        const int chunk = 2 * (DB * w + db) + (q >> 1);
         const int key0 = 32 * t + 4 * gq + e;
         const i32x2 lo = __builtin_bit_cast(i32x2, lds_tr16(vt + G::off(key0, chunk) + 8 * (q & 1)));
         const i32x2 hi = __builtin_bit_cast(i32x2, lds_tr16(vt + G::off(key0 + 16, chunk) + 8 * (q & 1)));
         const bf16x8 a = __builtin_bit_cast(bf16x8, i32x4{lo[0], lo[1], hi[0], hi[1]});
 #pragma unroll
-        for (int rb = 0; rb < 4; ++rb) {
-          o[4 * rb + db] = mfma_bf16(a, ph[rb], o[4 * rb + db]);
-          o[4 * rb + db] = mfma_bf16(a, pl[rb], o[4 * rb + db]);
+        for (int rb = 0; rb < NW; ++rb) {
+          o[DB * rb + db] = mfma_bf16(a, ph[rb], o[DB * rb + db]);
+          o[DB * rb + db] = mfma_bf16(a, pl[rb], o[DB * rb + db]);
         }
       }
       const bf16x8 ones = {(__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f,
@@ -307,12 +315,12 @@ __device__ __forceinline__ void pv_quarter(f32x4 (&o)[16], f32x4& lsum, const ld
   }
 }
 
-// The workgroup's 64 rows on one streamed tile.  qf, c2, klim, rs: this wave's
-// softmax rows (c2 includes the Q fragment's rscale; klim is the largest
+// The workgroup's 16 NW rows on one streamed tile.  qf, c2, klim, rs: this
+// wave's softmax rows (c2 includes the Q fragment's rscale; klim is the largest
 // visible key of this lane's row); min_lim: the smallest such limit over the
 // workgroup's rows (tiles entirely at or below it skip the mask); live: this
-// wave has live softmax rows; o: this wave's PV quarter.
-template <int QDT, int KV>
+// wave has live softmax rows; o, lsum: this wave's PV share.
+template <int QDT, int KV, int NW>
 struct SplitTile {
   const QFragT<KV>& qf;
   float c2;
@@ -321,7 +329,7 @@ struct SplitTile {
   RowStat& rs;
   f32x4 (&o)[16];
   f32x4& lsum;
-  Exchange<KV>& x;
+  Exchange<KV, NW>& x;
   __device__ __forceinline__ void front(const lds_t* kt, int tb) const {
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     if (live) {
@@ -337,15 +345,15 @@ struct SplitTile {
     }
   }
   __device__ __forceinline__ void back(const lds_t* vt, int) const {
-    pv_quarter<KV>(o, lsum, vt, x, __builtin_amdgcn_readfirstlane(threadIdx.x >> 6));
+    pv_quarter<KV, NW>(o, lsum, vt, x, __builtin_amdgcn_readfirstlane(threadIdx.x >> 6));
   }
 };
 
 // After the last tile: each wave publishes the sums of its softmax rows (0 for
-// a wave without live rows) so that every wave can normalise its PV quarter;
+// a wave without live rows) so that every wave can normalise its PV share;
 // returns this lane's row sum.  Contains a barrier.
-template <int KV>
-__device__ __forceinline__ float finish_rows(const f32x4& lsum, bool live, Exchange<KV>& x) {
+template <int KV, int NW>
+__device__ __forceinline__ float finish_rows(const f32x4& lsum, bool live, Exchange<KV, NW>& x) {
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = lane_id();
   const float lrow = live ? lsum[0] : 0.f;
@@ -354,34 +362,40 @@ __device__ __forceinline__ float finish_rows(const f32x4& lsum, bool live, Excha
   return lrow;
 }
 
-// Row rb of this wave's PV quarter times `scale`, written to a row of 256
-// head dimensions: bf16 (output) or fp32 (partial).
-__device__ __forceinline__ void store_quarter_bf16(const f32x4 (&o)[16], int rb, float scale, uint16_t* row_base) {
+// Row block rb of this wave's PV share times `scale`, written to a row of 256
+// head dimensions: bf16 (output), fp16 or fp32 (partials).
+template <int NW>
+__device__ __forceinline__ void store_share_bf16(const f32x4 (&o)[16], int rb, float scale, uint16_t* row_base) {
+  constexpr int DB = 16 / NW;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int gq = lane_id() >> 4;
 #pragma unroll
-  for (int db = 0; db < 4; ++db) {
-    const f32x4 v = o[4 * rb + db];
-    *reinterpret_cast<uint2*>(row_base + 64 * w + 16 * db + 4 * gq) =
+  for (int db = 0; db < DB; ++db) {
+    const f32x4 v = o[DB * rb + db];
+    *reinterpret_cast<uint2*>(row_base + (256 / NW) * w + 16 * db + 4 * gq) =
         make_uint2(pack_bf16x2(v[0] * scale, v[1] * scale), pack_bf16x2(v[2] * scale, v[3] * scale));
   }
 }
-__device__ __forceinline__ void store_quarter_f16(const f32x4 (&o)[16], int rb, float scale, uint16_t* row_base) {
+template <int NW>
+__device__ __forceinline__ void store_share_f16(const f32x4 (&o)[16], int rb, float scale, uint16_t* row_base) {
+  constexpr int DB = 16 / NW;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int gq = lane_id() >> 4;
 #pragma unroll
-  for (int db = 0; db < 4; ++db) {
-    const f32x4 v = o[4 * rb + db] * scale;
+  for (int db = 0; db < DB; ++db) {
+    const f32x4 v = o[DB * rb + db] * scale;
     const f16x4 h = {(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
-    *reinterpret_cast<f16x4*>(row_base + 64 * w + 16 * db + 4 * gq) = h;
+    *reinterpret_cast<f16x4*>(row_base + (256 / NW) * w + 16 * db + 4 * gq) = h;
   }
 }
-__device__ __forceinline__ void store_quarter_f32(const f32x4 (&o)[16], int rb, float scale, float* row_base) {
+template <int NW>
+__device__ __forceinline__ void store_share_f32(const f32x4 (&o)[16], int rb, float scale, float* row_base) {
+  constexpr int DB = 16 / NW;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int gq = lane_id() >> 4;
 #pragma unroll
-  for (int db = 0; db < 4; ++db)
-    *reinterpret_cast<f32x4*>(row_base + 64 * w + 16 * db + 4 * gq) = o[4 * rb + db] * scale;
+  for (int db = 0; db < DB; ++db)
+    *reinterpret_cast<f32x4*>(row_base + (256 / NW) * w + 16 * db + 4 * gq) = o[DB * rb + db] * scale;
 }
 
 // Q^T fragment of this lane's query row (lane % 16 of the wave), complete on

@@ -108,7 +108,7 @@ __device__ PlanPos plan_scan(const VerifyArgs& a, int num_wg, int target_t, int 
 
 template <int KV>
 __global__ __launch_bounds__(256, (KV == kFP8) ? 2 : 1) void verify_kernel(VerifyArgs a) {
-  __shared__ CausalSmem<KV> sm;
+  __shared__ CausalSmem<KV, 4> sm;
   __shared__ int plan_lds[5];
   const int wg = blockIdx.x, num_wg = gridDim.x;
   const int hkv = a.kv.num_kv_heads;
@@ -179,7 +179,7 @@ __global__ __launch_bounds__(256, (KV == kFP8) ? 2 : 1) void verify_kernel(Verif
     const bool live = 16 * w < rows;
     const int k_lo = lt0 * 64, k_hi = min(lt1 * 64, lk);
     const int32_t* bt_row = a.kv.bt + (int64_t)b * a.kv.bt_stride;
-    const int2 first = first_pages(a.kv, bt_row, k_lo, k_hi);
+    const int2 first = first_pages<4>(a.kv, bt_row, k_lo, k_hi);
     QFragT<KV> qf;
     load_q<kBF16, KV>(qf, a.q, tok, a.hq, head, row_ok);
     const int klim = row_ok ? min(lk - lq + t, k_hi - 1) : -1;
@@ -191,7 +191,7 @@ __global__ __launch_bounds__(256, (KV == kFP8) ? 2 : 1) void verify_kernel(Verif
     for (int i = 0; i < 16; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
     f32x4 lsum = {0.f, 0.f, 0.f, 0.f};
     stream_keys(sm, a.kv, bt_row, g, k_lo, k_hi, first,
-                SplitTile<kBF16, KV>{qf, c2 * qf.rscale, klim, min_lim, live, rs, o, lsum, sm.x});
+                SplitTile<kBF16, KV, 4>{qf, c2 * qf.rscale, klim, min_lim, live, rs, o, lsum, sm.x});
     const float lrow = finish_rows(lsum, live, sm.x);
     // A run that covers a whole uncut unit writes the output; any other piece
     // writes its normalised fp32 rows and their lse to its workspace slot.
@@ -212,12 +212,12 @@ __global__ __launch_bounds__(256, (KV == kFP8) ? 2 : 1) void verify_kernel(Verif
         const float inv = l > 0.f ? vds / l : 0.f;
         if (direct) {
           const int t2 = rr / a.r;
-          store_quarter_bf16(o, rb, inv, a.out + ((tok0 + t2) * (int64_t)a.hq + g * a.r + rr - t2 * a.r) * kHeadDim);
+          store_share_bf16<4>(o, rb, inv, a.out + ((tok0 + t2) * (int64_t)a.hq + g * a.r + rr - t2 * a.r) * kHeadDim);
         } else if constexpr (KV == kFP8) {
-          store_quarter_f16(o, rb, l > 0.f ? 1.f / l : 0.f,
+          store_share_f16<4>(o, rb, l > 0.f ? 1.f / l : 0.f,
                             static_cast<uint16_t*>(a.ws_o) + (slot * a.rows_cap + rr) * kHeadDim);
         } else {
-          store_quarter_f32(o, rb, l > 0.f ? 1.f / l : 0.f,
+          store_share_f32<4>(o, rb, l > 0.f ? 1.f / l : 0.f,
                             static_cast<float*>(a.ws_o) + (slot * a.rows_cap + rr) * kHeadDim);
         }
       }
