@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define PGA_ABI_VERSION 1
+#define PGA_ABI_VERSION 2
 #define PGA_HEAD_DIM 256
 
 /* Element encodings. */
@@ -200,6 +200,15 @@ int paged_attn_prefill_prefix(const void* q, int32_t q_dtype, const float* q_des
  *   seq_lens_k    [num_seqs] int32; block_table_stride must cover each Lk_b
  *   indices       [num_q_tokens, index_stride] int32
  *   num_selected  entries read per row, 0 <= num_selected <= index_stride
+ *   workspace     when few rows would leave the GPU idle (the launch profile
+ *                 changes with the row count on the page: Overview, Measured
+ *                 results), each row's list is cut into
+ *                 sparse_paged_attn_splits() pieces, attended by separate
+ *                 waves and merged by log-sum-exp; the pieces' rows and lse
+ *                 values live in this caller-owned device buffer of at least
+ *                 sparse_paged_attn_workspace_bytes() bytes, 256-byte aligned.
+ *                 NULL with workspace_bytes 0 asks for the unsplit launch
+ *                 (same result); a smaller non-empty buffer is an error.
  *   out           [num_q_tokens, num_q_heads, 256] bf16;  lse  [num_q_tokens, num_q_heads] fp32 or NULL
  * The pool must hold fewer than 2^31 tokens (num_pages * page_size).
  * Returns PGA_OK or a PGA_ERR_* code.
@@ -207,7 +216,16 @@ int paged_attn_prefill_prefix(const void* q, int32_t q_dtype, const float* q_des
 int sparse_paged_attn(const void* q, int32_t q_dtype, const float* q_descale, int32_t num_q_heads,
                       int32_t num_q_tokens, int32_t num_seqs, const int32_t* cu_seqlens_q, const int32_t* seq_lens_k,
                       const int32_t* indices, int64_t index_stride, int32_t num_selected, const pga_paged_kv* kv,
-                      float softmax_scale, void* out, float* lse, void* stream);
+                      float softmax_scale, void* workspace, size_t workspace_bytes, void* out, float* lse,
+                      void* stream);
+
+/* Pieces each row's index list is cut into for these host arguments (1: no
+ * split, no workspace needed), and the workspace that needs; 0 for invalid
+ * arguments. */
+int32_t sparse_paged_attn_splits(int32_t num_q_heads, int32_t num_kv_heads, int32_t num_q_tokens,
+                                 int32_t num_selected);
+size_t sparse_paged_attn_workspace_bytes(int32_t num_q_heads, int32_t num_kv_heads, int32_t num_q_tokens,
+                                         int32_t num_selected);
 
 /* Human-readable text of a status code (static storage). */
 const char* pga_status_string(int status);

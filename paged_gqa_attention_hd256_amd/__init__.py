@@ -19,7 +19,8 @@ from typing import Optional
 import torch
 
 __all__ = [
-    "PagedKV", "paged_attn_verify", "paged_attn_prefill_prefix", "sparse_paged_attn",
+    "PagedKV", "paged_attn_verify", "paged_attn_prefill_prefix", "sparse_paged_attn", "sparse_splits",
+    "sparse_workspace_bytes",
     "verify_workspace_bytes", "verify_split_tokens", "status_string", "abi_version", "library_path",
     "PagedGQAError", "LibraryNotBuilt", "load_library",
 ]
@@ -80,8 +81,12 @@ def load_library():
             lib.paged_attn_verify_split_tokens.restype = I32
             lib.paged_attn_prefill_prefix.argtypes = [P, I32, P, I32, I32, P, P, I32, I32, KVP, F, P, P, P]
             lib.paged_attn_prefill_prefix.restype = ctypes.c_int
-            lib.sparse_paged_attn.argtypes = [P, I32, P, I32, I32, I32, P, P, P, I64, I32, KVP, F, P, P, P]
+            lib.sparse_paged_attn.argtypes = [P, I32, P, I32, I32, I32, P, P, P, I64, I32, KVP, F, P, SZ, P, P, P]
             lib.sparse_paged_attn.restype = ctypes.c_int
+            lib.sparse_paged_attn_splits.argtypes = [I32, I32, I32, I32]
+            lib.sparse_paged_attn_splits.restype = I32
+            lib.sparse_paged_attn_workspace_bytes.argtypes = [I32, I32, I32, I32]
+            lib.sparse_paged_attn_workspace_bytes.restype = SZ
             lib.pga_status_string.argtypes = [ctypes.c_int]
             lib.pga_status_string.restype = ctypes.c_char_p
             lib.pga_abi_version.argtypes = []
@@ -228,18 +233,37 @@ def paged_attn_prefill_prefix(q, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, 
     return out
 
 
+def sparse_splits(num_q_heads: int, num_kv_heads: int, num_q_tokens: int, num_selected: int) -> int:
+    return load_library().sparse_paged_attn_splits(num_q_heads, num_kv_heads, num_q_tokens, num_selected)
+
+
+def sparse_workspace_bytes(num_q_heads: int, num_kv_heads: int, num_q_tokens: int, num_selected: int) -> int:
+    return load_library().sparse_paged_attn_workspace_bytes(num_q_heads, num_kv_heads, num_q_tokens, num_selected)
+
+
 def sparse_paged_attn(q, cu_seqlens_q, seq_lens_k, indices, kv: PagedKV, softmax_scale: float,
-                      num_selected: Optional[int] = None, q_descale=None, out=None, lse=None, stream=None):
-    """Selected-token attention; ``indices`` is int32 [T, W]; returns ``out``."""
+                      num_selected: Optional[int] = None, q_descale=None, workspace=None, out=None, lse=None,
+                      stream=None, split: bool = True):
+    """Selected-token attention; ``indices`` is int32 [T, W]; returns ``out``.
+    With ``split`` (the default) the library may cut each row's list into
+    pieces when there are few rows; ``workspace`` is then allocated here
+    unless given.  ``split=False`` asks for the unsplit launch."""
     lib = load_library()
     out = _out(q, out)
     s = kv._struct()
     if indices.dtype != torch.int32 or indices.dim() != 2 or indices.stride(1) != 1:
         raise ValueError("indices must be a row-major int32 [T, W] tensor")
     ns = indices.shape[1] if num_selected is None else num_selected
+    if not split:
+        workspace = None
+    elif workspace is None:
+        need = sparse_workspace_bytes(q.shape[1], kv.num_kv_heads, q.shape[0], ns)
+        if need > 0:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     st = lib.sparse_paged_attn(q.data_ptr(), _dtype_code(q), _ptr(q_descale), q.shape[1], q.shape[0],
                                seq_lens_k.shape[0], cu_seqlens_q.data_ptr(), seq_lens_k.data_ptr(),
                                indices.data_ptr(), indices.stride(0), ns, ctypes.byref(s), float(softmax_scale),
+                               _ptr(workspace), 0 if workspace is None else workspace.numel() * workspace.element_size(),
                                out.data_ptr(), _ptr(lse), _stream(stream))
     _check("sparse_paged_attn", st)
     return out

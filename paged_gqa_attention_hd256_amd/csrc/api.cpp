@@ -133,6 +133,36 @@ int launch_status(hipError_t e) { return e == hipSuccess ? PGA_OK : PGA_ERR_LAUN
 
 }  // namespace
 
+// Sparse split plan from the host arguments alone.  When the rows' jobs
+// (query token x kv head x 16-row block) would not fill the GPU, each row's
+// index list is cut into pieces (multiples of 32 entries, at least 256 per
+// piece, at most kMaxSparseSplits), processed by separate waves and merged by
+// log-sum-exp.
+constexpr int64_t kSparseTargetJobs = 4096;  // ~4 waves per SIMD of a 256-CU device
+constexpr int32_t kMaxSparseSplits = 32;
+struct SparsePlan {
+  int32_t splits = 1, split_len = 1;
+  size_t ws_o_bytes = 0, ws_bytes = 0;
+};
+bool plan_sparse(int32_t hq, int32_t hkv, int32_t num_q_tokens, int32_t num_selected, SparsePlan& p) {
+  if (hq <= 0 || hkv <= 0 || hq % hkv != 0 || num_q_tokens < 0 || num_selected < 0) return false;
+  const int64_t jobs = int64_t(num_q_tokens) * hkv * cdiv(hq / hkv, 16);
+  int64_t splits = 1;
+  if (jobs > 0 && jobs < kSparseTargetJobs && num_selected > 0)
+    splits = std::max<int64_t>(1, std::min<int64_t>({cdiv(kSparseTargetJobs, jobs), kMaxSparseSplits,
+                                                     cdiv(num_selected, 256)}));
+  const int64_t len = std::max<int64_t>(32, (cdiv(num_selected, splits) + 31) / 32 * 32);
+  p.splits = num_selected > 0 ? static_cast<int32_t>(cdiv(num_selected, len)) : 1;
+  p.split_len = static_cast<int32_t>(len);
+  p.ws_o_bytes = p.ws_bytes = 0;
+  if (p.splits > 1) {
+    const size_t slots = size_t(num_q_tokens) * hq * p.splits;
+    p.ws_o_bytes = (slots * kHeadDim * sizeof(float) + 255) & ~size_t(255);
+    p.ws_bytes = p.ws_o_bytes + slots * sizeof(float);
+  }
+  return true;
+}
+
 extern "C" {
 
 int pga_abi_version(void) { return PGA_ABI_VERSION; }
@@ -302,7 +332,8 @@ int paged_attn_prefill_prefix(const void* q, int32_t q_dtype, const float* q_des
 int sparse_paged_attn(const void* q, int32_t q_dtype, const float* q_descale, int32_t num_q_heads,
                       int32_t num_q_tokens, int32_t num_seqs, const int32_t* cu_seqlens_q, const int32_t* seq_lens_k,
                       const int32_t* indices, int64_t index_stride, int32_t num_selected, const pga_paged_kv* kv,
-                      float softmax_scale, void* out, float* lse, void* stream) {
+                      float softmax_scale, void* workspace, size_t workspace_bytes, void* out, float* lse,
+                      void* stream) {
   if (!q || !cu_seqlens_q || !seq_lens_k || !out || !kv) return PGA_ERR_NULL;
   if (num_selected > 0 && !indices) return PGA_ERR_NULL;
   if (num_seqs < 0 || num_q_heads <= 0 || num_q_tokens < 0 || num_selected < 0 || index_stride < num_selected)
@@ -314,6 +345,18 @@ int sparse_paged_attn(const void* q, int32_t q_dtype, const float* q_descale, in
   if (int64_t(kv->num_pages) * kv->page_size > INT32_MAX) return PGA_ERR_UNSUPPORTED;
   if (!aligned(q, 16) || !aligned(out, 8) || (lse && !aligned(lse, 4))) return PGA_ERR_UNSUPPORTED;
   if (num_selected > 0 && !aligned(indices, 4)) return PGA_ERR_UNSUPPORTED;
+  SparsePlan plan;
+  if (!plan_sparse(num_q_heads, kv->num_kv_heads, num_q_tokens, num_selected, plan)) return PGA_ERR_SHAPE;
+  if (plan.splits > 1) {
+    if (!workspace && workspace_bytes == 0) {
+      plan.splits = 1;  // the caller asked for the unsplit launch
+      plan.split_len = std::max(num_selected, 1);
+    } else if (!workspace || workspace_bytes < plan.ws_bytes) {
+      return PGA_ERR_WORKSPACE;
+    } else if (!aligned(workspace, 256)) {
+      return PGA_ERR_UNSUPPORTED;
+    }
+  }
   if (num_q_tokens == 0) return PGA_OK;
 
   pga::SparseArgs a{};
@@ -332,7 +375,25 @@ int sparse_paged_attn(const void* q, int32_t q_dtype, const float* q_descale, in
   a.c2_base = softmax_scale * 1.4426950408889634f;
   a.out = static_cast<uint16_t*>(out);
   a.lse = lse;
+  a.splits = plan.splits;
+  a.split_len = plan.split_len;
+  if (plan.splits > 1) {
+    a.ws_o = workspace;
+    a.ws_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.ws_o_bytes);
+  }
   return launch_status(pga::launch_sparse(a, kv->dtype, static_cast<hipStream_t>(stream)));
+}
+
+size_t sparse_paged_attn_workspace_bytes(int32_t num_q_heads, int32_t num_kv_heads, int32_t num_q_tokens,
+                                         int32_t num_selected) {
+  SparsePlan p;
+  return plan_sparse(num_q_heads, num_kv_heads, num_q_tokens, num_selected, p) ? p.ws_bytes : 0;
+}
+
+int32_t sparse_paged_attn_splits(int32_t num_q_heads, int32_t num_kv_heads, int32_t num_q_tokens,
+                                 int32_t num_selected) {
+  SparsePlan p;
+  return plan_sparse(num_q_heads, num_kv_heads, num_q_tokens, num_selected, p) ? p.splits : 0;
 }
 
 }  // extern "C"

@@ -74,6 +74,11 @@ struct SparseArgs {
   float c2_base;
   uint16_t* out;
   float* lse;
+  int32_t splits;          // pieces each row's list is cut into (1: no split, output written directly)
+  int32_t split_len;       // list entries per piece (a multiple of 32)
+  void* ws_o;              // [T * hq * splits, 256] partial rows over their row sums, V code units:
+                           // fp16 for FP8 V, fp32 for BF16 V
+  float* ws_lse;           // [T * hq * splits] natural-log lse of the pieces
 };
 
 // Launchers (defined next to their kernels).  They return the launch status.

@@ -55,11 +55,14 @@ __global__ __launch_bounds__(SparseCfg<KV>::kWaves * 64) void sparse_kernel(Spar
   const int lane = lane_id();
   const int n = lane & 15, gq = lane >> 4;
   const int nrb = (a.r + 15) >> 4;                  // 16-row blocks per kv group
+  const int S = a.splits;
   const int64_t job = (int64_t)blockIdx.x * C::kWaves + w;
-  const int64_t njobs = (int64_t)a.num_tokens * a.kv.num_kv_heads * nrb;
+  const int64_t njobs = (int64_t)a.num_tokens * a.kv.num_kv_heads * nrb * S;
   if (job >= njobs) return;
-  const int tok = (int)(job / (a.kv.num_kv_heads * nrb));
-  const int rem = (int)(job - (int64_t)tok * a.kv.num_kv_heads * nrb);
+  const int64_t rowjob = job / S;
+  const int sp = (int)(job - rowjob * S);  // piece of the row's index list
+  const int tok = (int)(rowjob / (a.kv.num_kv_heads * nrb));
+  const int rem = (int)(rowjob - (int64_t)tok * a.kv.num_kv_heads * nrb);
   const int g = rem / nrb, rb = rem - (rem / nrb) * nrb;
   const int b = seq_of(a.cu_q, a.num_seqs, tok);
   const int lk = a.lens_k[b];
@@ -83,8 +86,9 @@ __global__ __launch_bounds__(SparseCfg<KV>::kWaves * 64) void sparse_kernel(Spar
   WaveState st;
   st.init();
 
-  for (int c0 = 0; c0 < a.num_selected; c0 += kSparseTableEntries) {
-    const int cnt = min(kSparseTableEntries, a.num_selected - c0);
+  const int e_end = min((sp + 1) * a.split_len, a.num_selected);
+  for (int c0 = sp * a.split_len; c0 < e_end; c0 += kSparseTableEntries) {
+    const int cnt = min(kSparseTableEntries, e_end - c0);
     const int ntiles = (cnt + C::kTileKeys - 1) / C::kTileKeys;
     // Translate this chunk's entries (and pad the last tile) into physical rows.
     for (int e = lane; e < ntiles * C::kTileKeys; e += 64) {
@@ -145,6 +149,22 @@ __global__ __launch_bounds__(SparseCfg<KV>::kWaves * 64) void sparse_kernel(Spar
 
   const float lrow = group4_sum(st.l);
   if (!row_ok) return;
+  if (S > 1) {  // a piece of the row: rows over their sums (V code units) and lse, merged later
+    const int64_t slot = ((int64_t)tok * a.hq + head) * S + sp;
+    const float inv = lrow > 0.f ? 1.f / lrow : 0.f;
+#pragma unroll
+    for (int mb = 0; mb < 16; ++mb) {
+      const f32x4 v = st.o[mb] * inv;
+      if constexpr (KV == kFP8) {
+        const f16x4 h = {(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
+        *reinterpret_cast<f16x4*>(static_cast<uint16_t*>(a.ws_o) + slot * kHeadDim + 16 * mb + 4 * gq) = h;
+      } else {
+        *reinterpret_cast<f32x4*>(static_cast<float*>(a.ws_o) + slot * kHeadDim + 16 * mb + 4 * gq) = v;
+      }
+    }
+    if (gq == 0) a.ws_lse[slot] = lrow > 0.f ? (st.m + log2f(lrow)) * kLn2 : kNegInf;
+    return;
+  }
   const float vds = load_scale(a.kv.v_ds);
   const float inv = lrow > 0.f ? vds / lrow : 0.f;
   uint16_t* op = a.out + ((int64_t)tok * a.hq + head) * kHeadDim + 4 * gq;
@@ -157,15 +177,68 @@ __global__ __launch_bounds__(SparseCfg<KV>::kWaves * 64) void sparse_kernel(Spar
   if (gq == 0 && a.lse) a.lse[(int64_t)tok * a.hq + head] = lrow > 0.f ? (st.m + log2f(lrow)) * kLn2 : kNegInf;
 }
 
+// Log-sum-exp merge of the pieces of each (query token, head) row: one wave
+// per row, the lse of up to 64 pieces read one per lane, the rows of 8 pieces
+// in flight at a time; pieces with lse = -inf (no visible entry) get weight 0.
+template <int KV>
+__global__ __launch_bounds__(256) void sparse_merge_kernel(SparseArgs a) {
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // token * hq + head
+  if (row >= (int64_t)a.num_tokens * a.hq) return;
+  const int lane = lane_id();
+  const int S = a.splits;
+  const float ls = lane < S ? a.ws_lse[row * S + lane] : kNegInf;
+  const float mx = wave_max(ls);
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  float wsum = 0.f;
+  if (mx != kNegInf) {
+    const float wgt = ls == kNegInf ? 0.f : __expf(ls - mx);
+    wsum = wave_sum(wgt);
+    auto part = [&](int sl) -> f32x4 {
+      const int64_t off = (row * S + sl) * kHeadDim + 4 * lane;
+      if constexpr (KV == kFP8) {
+        const f16x4 h = *reinterpret_cast<const f16x4*>(static_cast<const uint16_t*>(a.ws_o) + off);
+        return f32x4{(float)h[0], (float)h[1], (float)h[2], (float)h[3]};
+      } else {
+        return *reinterpret_cast<const f32x4*>(static_cast<const float*>(a.ws_o) + off);
+      }
+    };
+    for (int s0 = 0; s0 < S; s0 += 8) {
+      f32x4 v[8];
+      float wq[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int sk = min(s0 + k, S - 1);
+        wq[k] = s0 + k < S ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wgt), min(s0 + k, 63))) : 0.f;
+        v[k] = part(sk);
+      }
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        if (wq[k] != 0.f) acc += wq[k] * v[k];
+    }
+  }
+  const float inv = wsum > 0.f ? load_scale(a.kv.v_ds) / wsum : 0.f;
+  uint16_t* op = a.out + row * kHeadDim + 4 * lane;
+  *reinterpret_cast<uint2*>(op) = make_uint2(pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv));
+  if (lane == 0 && a.lse) a.lse[row] = wsum > 0.f ? mx + logf(wsum) : kNegInf;
+}
+
 hipError_t launch_sparse(const SparseArgs& a, int kv_dtype, hipStream_t s) {
   const int nrb = (a.r + 15) / 16;
-  const int64_t jobs = (int64_t)a.num_tokens * a.kv.num_kv_heads * nrb;
-  if (kv_dtype == kFP8) {
-    constexpr int W = SparseCfg<kFP8>::kWaves;
-    hipLaunchKernelGGL(sparse_kernel<kFP8>, dim3((unsigned)((jobs + W - 1) / W)), dim3(W * 64), 0, s, a);
-  } else {
-    constexpr int W = SparseCfg<kBF16>::kWaves;
-    hipLaunchKernelGGL(sparse_kernel<kBF16>, dim3((unsigned)((jobs + W - 1) / W)), dim3(W * 64), 0, s, a);
+  const int64_t jobs = (int64_t)a.num_tokens * a.kv.num_kv_heads * nrb * a.splits;
+  constexpr int W = 4;  // waves per workgroup, both encodings
+  static_assert(SparseCfg<kFP8>::kWaves == W && SparseCfg<kBF16>::kWaves == W, "launch shape");
+  const dim3 grid((unsigned)((jobs + W - 1) / W));
+  if (kv_dtype == kFP8)
+    hipLaunchKernelGGL(sparse_kernel<kFP8>, grid, dim3(W * 64), 0, s, a);
+  else
+    hipLaunchKernelGGL(sparse_kernel<kBF16>, grid, dim3(W * 64), 0, s, a);
+  if (a.splits > 1) {
+    if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+    const dim3 mgrid((unsigned)(((int64_t)a.num_tokens * a.hq + 3) / 4));
+    if (kv_dtype == kFP8)
+      hipLaunchKernelGGL(sparse_merge_kernel<kFP8>, mgrid, dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL(sparse_merge_kernel<kBF16>, mgrid, dim3(256), 0, s, a);
   }
   return hipGetLastError();
 }

@@ -238,17 +238,6 @@ __global__ __launch_bounds__(256, (KV == kFP8) ? 2 : 1) void verify_kernel(Verif
   }
 }
 
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
-  return x;
-}
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off);
-  return x;
-}
-
 // Log-sum-exp merge of the partial rows of every (sequence, kv head) unit that
 // verify_kernel did not write directly.  One wave per query row: the lanes
 // take one piece each (the lse of up to 64 pieces in one load, their maximum

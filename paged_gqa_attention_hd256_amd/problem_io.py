@@ -15,7 +15,8 @@ from typing import Optional
 import numpy as np
 import torch
 
-from . import PagedKV, paged_attn_prefill_prefix, paged_attn_verify, sparse_paged_attn, verify_workspace_bytes
+from . import (PagedKV, paged_attn_prefill_prefix, paged_attn_verify, sparse_paged_attn, sparse_workspace_bytes,
+               verify_workspace_bytes)
 
 
 def _codes_to_tensor(codes: np.ndarray, dtype: str, device) -> torch.Tensor:
@@ -76,6 +77,10 @@ def to_device(p, device="cuda", kv_split_tokens: Optional[int] = None) -> Device
         need = verify_workspace_bytes(Hq, kv.num_kv_heads, len(p.seq_lens_k), max(1, max_q), max_k, split)
         if need:
             ws = torch.empty(need, dtype=torch.uint8, device=device)
+    if p.mode == "sparse" and idx is not None:
+        need = sparse_workspace_bytes(Hq, kv.num_kv_heads, T, idx.shape[1])
+        if need:
+            ws = torch.empty(need, dtype=torch.uint8, device=device)
     q_ds = _scalar(p.q_descale, device) if p.q_dtype != "bf16" else None
     return DeviceProblem(p.mode, q, q_ds, cu_q, lens_k, cu_k, kv, float(p.softmax_scale), max_q, max_k, split, idx,
                          out, lse, ws)
@@ -83,7 +88,8 @@ def to_device(p, device="cuda", kv_split_tokens: Optional[int] = None) -> Device
 
 def run(dp: DeviceProblem, stream=None, stage: str = "all") -> torch.Tensor:
     """One call of the entry point matching ``dp.mode``; writes dp.out / dp.lse.
-    For verify, ``stage`` may select only the attention kernel or only the merge."""
+    For verify, ``stage`` may select only the attention kernel or only the merge;
+    for sparse, ``stage="unsplit"`` asks for the launch without list pieces."""
     if dp.mode == "verify":
         return paged_attn_verify(dp.q, dp.cu_seqlens_q, dp.seq_lens_k, dp.max_q_len, dp.max_kv_len, dp.kv,
                                  dp.softmax_scale, dp.kv_split_tokens, q_descale=dp.q_descale, workspace=dp.workspace,
@@ -94,5 +100,6 @@ def run(dp: DeviceProblem, stream=None, stage: str = "all") -> torch.Tensor:
                                          stream=stream)
     if dp.mode == "sparse":
         return sparse_paged_attn(dp.q, dp.cu_seqlens_q, dp.seq_lens_k, dp.indices, dp.kv, dp.softmax_scale,
-                                 q_descale=dp.q_descale, out=dp.out, lse=dp.lse, stream=stream)
+                                 q_descale=dp.q_descale, workspace=dp.workspace, out=dp.out, lse=dp.lse, stream=stream,
+                                 split=stage != "unsplit")
     raise ValueError(dp.mode)

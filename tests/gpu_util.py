@@ -11,7 +11,7 @@ REL_L2 = 2e-3
 LSE_ABS = 1e-3
 
 
-def run_gpu(p, split=None, repeat=1):
+def run_gpu(p, split=None, repeat=1, stage="all"):
     import torch
     from paged_gqa_attention_hd256_amd import problem_io
 
@@ -20,7 +20,7 @@ def run_gpu(p, split=None, repeat=1):
     for _ in range(repeat):
         dp.out.fill_(float("nan"))
         dp.lse.fill_(float("nan"))
-        problem_io.run(dp)
+        problem_io.run(dp, stage=stage)
         torch.cuda.synchronize()
         outs.append((dp.out.view(torch.int16).cpu().numpy().copy(), dp.lse.cpu().numpy().copy()))
     return outs if repeat > 1 else outs[0]

@@ -36,7 +36,7 @@ def test_library_exports_every_declared_function(lib):
     assert {"paged_attn_verify", "paged_attn_prefill_prefix", "sparse_paged_attn"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.pga_abi_version() == 1
+    assert lib.pga_abi_version() == 2
 
 
 def test_status_strings(lib):
@@ -156,12 +156,12 @@ def test_prefill_rejects_invalid_arguments(lib):
 
 def sparse(lib, kv=None, **kw):
     a = dict(q=P(), q_dtype=1, qds=None, hq=24, ntok=8, nseq=1, cuq=P(16384), lk=P(16384 + 64), idx=P(30000),
-             stride=64, nsel=64, scale=0.0625, out=P(20000), lse=None)
+             stride=64, nsel=64, scale=0.0625, ws=None, wsb=0, out=P(20000), lse=None)
     a.update(kw)
     kv = kv or kv_struct(num_kv_heads=2)
     return lib.sparse_paged_attn(a["q"], a["q_dtype"], a["qds"], a["hq"], a["ntok"], a["nseq"], a["cuq"], a["lk"],
-                                 a["idx"], a["stride"], a["nsel"], ctypes.byref(kv), a["scale"], a["out"], a["lse"],
-                                 None)
+                                 a["idx"], a["stride"], a["nsel"], ctypes.byref(kv), a["scale"], a["ws"], a["wsb"],
+                                 a["out"], a["lse"], None)
 
 
 def test_sparse_rejects_invalid_arguments(lib):
@@ -173,3 +173,31 @@ def test_sparse_rejects_invalid_arguments(lib):
     assert sparse(lib, hq=25) == ESHAPE
     assert sparse(lib, kv=kv_struct(num_kv_heads=2, num_pages=1 << 30, page_size=64)) == EUNSUP
     assert sparse(lib, ntok=0) == OK
+    # 8 rows x 2 kv heads leave the GPU idle: the lists are cut into pieces,
+    # which need a workspace of the reported size and alignment.
+    assert sparse(lib, nsel=2048, stride=2048, ws=P(1 << 20), wsb=16) == EWS
+    assert sparse(lib, nsel=2048, stride=2048, ws=P((1 << 20) + 4), wsb=1 << 40) == EUNSUP
+
+
+def test_sparse_split_plan(lib):
+    def expect(hq, hkv, ntok, nsel):
+        jobs = ntok * hkv * -(-(hq // hkv) // 16)
+        splits = 1
+        if 0 < jobs < 4096 and nsel > 0:
+            splits = max(1, min(-(-4096 // jobs), 32, -(-nsel // 256)))
+        length = max(32, -(-(-(-nsel // splits)) // 32) * 32)
+        splits = -(-nsel // length) if nsel > 0 else 1
+        ws = 0
+        if splits > 1:
+            slots = ntok * hq * splits
+            ws = ((slots * 256 * 4 + 255) & ~255) + slots * 4
+        return splits, ws
+
+    for args in [(24, 2, 8, 2048), (24, 2, 8192, 2051), (24, 2, 260, 2051), (12, 1, 3, 100), (32, 1, 1, 5000),
+                 (24, 2, 0, 2051), (24, 2, 10, 0)]:
+        splits, ws = expect(*args)
+        assert lib.sparse_paged_attn_splits(*args) == splits, args
+        assert lib.sparse_paged_attn_workspace_bytes(*args) == ws, args
+    assert lib.sparse_paged_attn_splits(24, 2, 8, 2048) == 8
+    assert lib.sparse_paged_attn_splits(24, 2, 8192, 2051) == 1      # the large-row workload: no split
+    assert lib.sparse_paged_attn_splits(25, 2, 8, 64) == 0          # invalid head counts

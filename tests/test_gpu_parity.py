@@ -148,6 +148,53 @@ def test_sparse_index_handling_bit_exact(kv_dtype):
         assert np.array_equal(bf16_bits_to_f64(bits[t]), expect)
 
 
+SPARSE_SMALL_CASES = [
+    ("fp8_4rows_2051", dict(seed=[51], lq=[4], lk=[5000], hq=24, hkv=2, n=2051, kv=w.FP8)),
+    ("bf16_4rows_2051", dict(seed=[52], lq=[4], lk=[5000], hq=24, hkv=2, n=2051, kv=w.BF16)),
+    ("fp8_2seq_600", dict(seed=[53], lq=[3, 2], lk=[3000, 1400], hq=12, hkv=1, n=600, kv=w.FP8)),
+    ("bf16_32to1_1000", dict(seed=[54], lq=[2], lk=[4000], hq=32, hkv=1, n=1000, kv=w.BF16)),
+]
+
+
+@pytest.mark.parametrize("name,c", SPARSE_SMALL_CASES, ids=[n for n, _ in SPARSE_SMALL_CASES])
+@pytest.mark.parametrize("pad", [0.0, 0.5])
+def test_sparse_small_rows_split_and_unsplit(name, c, pad):
+    """Few rows: each row's list is cut into pieces merged by log-sum-exp; the
+    split and the unsplit launch both meet the bar against the oracle."""
+    import paged_gqa_attention_hd256_amd as pga
+
+    p = w.poison_unused(_sparse_problem(name, c, pad))
+    assert pga.sparse_splits(p.num_q_heads, p.num_kv_heads, p.num_tokens, p.indices.shape[1]) > 1
+    ref, ref_lse = oracle.attention(p)
+    for stage in ["all", "unsplit"]:
+        bits, lse = run_gpu(p, stage=stage)
+        assert_parity(bits, lse, ref, ref_lse, what=f"{name}/pad{pad}/{stage}")
+
+
+@pytest.mark.parametrize("kv_dtype", [w.BF16, w.FP8])
+def test_sparse_split_index_handling_bit_exact(kv_dtype):
+    """One valid entry among 700 (the rest padding): the list is cut into
+    pieces, all but one without a visible entry, and the merged row must still
+    be RNE(v_ds * V_j) bitwise."""
+    import paged_gqa_attention_hd256_amd as pga
+
+    p = w.make_sparse("one_of_700", [55], [8], [1600], 24, 2, 1, kv_dtype=kv_dtype, width=700)
+    assert pga.sparse_splits(24, 2, 8, 700) > 1
+    if kv_dtype == w.FP8:
+        p.v_descale = 0.25
+    rng = np.random.default_rng(7)
+    for t in range(8):  # move the one valid entry to a random column
+        j = p.indices[t, 0]
+        p.indices[t, :] = -1
+        p.indices[t, rng.integers(0, 700)] = j
+    bits, _ = run_gpu(p)
+    _, v = refs.logical_kv(p, 0)
+    for t in range(8):
+        j = p.indices[t][p.indices[t] >= 0][0]
+        expect = refs.bf16_round(np.repeat(v[j].numpy(), 12, axis=0))
+        assert np.array_equal(bf16_bits_to_f64(bits[t]), expect)
+
+
 # --------------------------------------------------- determinism, permutation ---
 @pytest.mark.parametrize("mode", ["verify", "prefill", "sparse"])
 def test_bitwise_determinism_and_page_permutation_invariance(mode):

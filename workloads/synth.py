@@ -301,6 +301,7 @@ _CONFIGS = {
     "prefix_prefill_128k": 4,
     "sparse_bf16": 5,
     "sparse_fp8": 5,
+    "sparse_fp8_260rows": 6,
 }
 
 
@@ -335,6 +336,10 @@ def config(name: str) -> Problem:
         sub = 0 if name.endswith("32k") else 1
         return make_causal(name, [c, sub], [16384], [lk], 8, 1, kv_dtype=FP8, q_dtype=FP8,
                            mode="prefill")
+    if name == "sparse_fp8_260rows":
+        # The few-row regime of the same selection: the last 260 rows of the
+        # 32768-token sequence, 24 q / 2 kv, 2051 selected tokens each, FP8 K/V.
+        return make_sparse(name, [c, 0], [260], [32768], 24, 2, 2051, kv_dtype=FP8)
     if name in ("sparse_bf16", "sparse_fp8"):
         # 8192 query rows at positions 24576..32767 of one 32768-token sequence, 24 q / 2 kv,
         # 2051 selected tokens per row; the same draws encoded as BF16 or FP8 K/V.
