@@ -68,6 +68,12 @@ def _lib():
             h.oracle_decode_bf16.restype = D
             h.oracle_decode_e4m3fn.argtypes = [ctypes.c_uint8]
             h.oracle_decode_e4m3fn.restype = D
+            h.oracle_encode_e4m3fn.argtypes = [ctypes.c_float]
+            h.oracle_encode_e4m3fn.restype = ctypes.c_uint8
+            h.oracle_quantize_fp8.argtypes = [P, I64, P, P, P]
+            h.oracle_quantize_fp8.restype = ctypes.c_int
+            h.oracle_write_new_kv.argtypes = [P, P, I32, P, P, ctypes.POINTER(_KV), ctypes.c_float, ctypes.c_float]
+            h.oracle_write_new_kv.restype = ctypes.c_int
             _handle = h
     return _handle
 
@@ -144,3 +150,40 @@ def decode_bf16(bits: int) -> float:
 
 def decode_e4m3fn(code: int) -> float:
     return _lib().oracle_decode_e4m3fn(code)
+
+
+def encode_e4m3fn(y: float) -> int:
+    """E4M3FN code nearest to the fp32 value ``y`` (ties to even, saturating)."""
+    return int(_lib().oracle_encode_e4m3fn(float(np.float32(y))))
+
+
+def quantize_fp8(x_bits: np.ndarray, descale=None):
+    """Per-tensor FP8 quantisation of bf16 patterns ``x_bits`` (any shape).
+
+    ``descale=None`` takes the dynamic scale amax/448; otherwise the given fp32
+    descale.  Returns (uint8 codes of the same shape, fp32 descale)."""
+    x = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    codes = np.empty(x.shape, dtype=np.uint8)
+    out = np.zeros(1, dtype=np.float32)
+    din = None if descale is None else np.array([descale], dtype=np.float32)
+    rc = _lib().oracle_quantize_fp8(_ptr(x), x.size, None if din is None else _ptr(din), _ptr(codes), _ptr(out))
+    if rc != 0:
+        raise ValueError("oracle rejected the quantisation (code %d)" % rc)
+    return codes, float(out[0])
+
+
+def write_new_kv(p, k_new: np.ndarray, v_new: np.ndarray, cu_seqlens_k: np.ndarray) -> None:
+    """Quantise the new tokens' keys and values (bf16 [T, Hkv, 256]) with the
+    pool's descales of problem ``p`` and write them into ``p``'s FP8 pools in
+    place, at logical positions Lk_b - Lq_b + t."""
+    k = np.ascontiguousarray(k_new, dtype=np.uint16)
+    v = np.ascontiguousarray(v_new, dtype=np.uint16)
+    cu_q = np.ascontiguousarray(p.cu_seqlens_q, dtype=np.int32)
+    cu_k = np.ascontiguousarray(cu_seqlens_k, dtype=np.int32)
+    assert p.k_cache.flags["C_CONTIGUOUS"] and p.v_cache.flags["C_CONTIGUOUS"]
+    kv = _kv(p)
+    rc = _lib().oracle_write_new_kv(_ptr(k), _ptr(v), p.num_seqs, _ptr(cu_q), _ptr(cu_k), ctypes.byref(kv),
+                                    float(np.float32(p.k_descale)), float(np.float32(p.v_descale)))
+    if rc != 0:
+        raise ValueError("oracle rejected the key/value write (code %d)" % rc)
+

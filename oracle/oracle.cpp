@@ -366,3 +366,114 @@ int oracle_causal_probs(const void* q, int32_t q_dtype, double q_descale, int32_
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Per-tensor FP8 quantisation of the prefill inputs: the casts of Q and of the
+// new keys and values to FP8 that ROCm/ATOM PR #2534 counts inside its prefill
+// timings (FMHA commit message; Results, per-layer trace).  The page fixes no
+// scale rule, so the oracle takes the plainest one, in the precision the
+// kernels use (fp32):
+//   amax    = max |x| over the non-NaN elements (exact: x is bf16)
+//   descale = fp32(amax / 448), or 1 when amax is 0 (dynamic scale, Q)
+//   y       = fp32(x / descale)
+//   code    = the E4M3FN value nearest to y, ties to the even code, with
+//             finite y beyond +-448 saturated to +-448 and NaN kept NaN.
+// New keys and values use the pool's own per-tensor descales (static scales:
+// the pool already holds the cached prefix under them) and land at logical
+// position Lk_b - Lq_b + t of their sequence, through the block table.
+
+namespace {
+
+// Codes 0x00 .. 0x7E are the finite non-negative E4M3FN values in increasing
+// order; a binary search over their decoded values finds the neighbours of |y|.
+uint8_t encode_e4m3fn(float y) {
+  if (std::isnan(y)) return std::signbit(y) ? 0xFF : 0x7F;
+  const uint8_t sign = std::signbit(y) ? 0x80 : 0x00;
+  const double a = std::fabs(static_cast<double>(y));
+  const E4M3Table& t = e4m3_table();
+  int lo = 0, hi = 0x7E;  // largest code c with value(c) <= a
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) / 2;
+    if (t.v[mid] <= a) lo = mid; else hi = mid - 1;
+  }
+  int c = lo;
+  if (c < 0x7E) {
+    const double below = a - t.v[c], above = t.v[c + 1] - a;  // exact in fp64
+    if (above < below || (above == below && (c & 1))) c += 1;
+  }
+  return static_cast<uint8_t>(sign | c);
+}
+
+float bf16_to_float(uint16_t bits) {
+  uint32_t w = static_cast<uint32_t>(bits) << 16;
+  float f;
+  std::memcpy(&f, &w, sizeof f);
+  return f;
+}
+
+uint8_t quantize_one(uint16_t bits, float descale) {
+  const float y = bf16_to_float(bits) / descale;  // one IEEE fp32 division
+  return encode_e4m3fn(y);
+}
+
+}  // namespace
+
+extern "C" {
+
+uint8_t oracle_encode_e4m3fn(float y) { return encode_e4m3fn(y); }
+
+// x: n bf16 patterns.  descale_in: NULL for the dynamic scale, else the fp32
+// descale to use.  codes: n bytes out.  descale_out: the descale used.
+int oracle_quantize_fp8(const uint16_t* x, int64_t n, const float* descale_in, uint8_t* codes,
+                        float* descale_out) {
+  if ((!x && n > 0) || (!codes && n > 0) || !descale_out || n < 0) return 1;
+  float descale;
+  if (descale_in) {
+    descale = *descale_in;
+  } else {
+    float amax = 0.0f;
+    for (int64_t i = 0; i < n; ++i) {
+      const float a = std::fabs(bf16_to_float(x[i]));
+      if (!std::isnan(a) && a > amax) amax = a;
+    }
+    descale = amax > 0.0f ? amax / 448.0f : 1.0f;
+  }
+  for (int64_t i = 0; i < n; ++i) codes[i] = quantize_one(x[i], descale);
+  *descale_out = descale;
+  return 0;
+}
+
+// Quantise the new tokens' keys and values ([T, Hkv, 256] bf16 each, token
+// order of cu_seqlens_q) with the given descales and write them into the FP8
+// pool of `kv` (its caches are written through) at logical positions
+// Lk_b - Lq_b + t, Lk_b = cu_seqlens_k[b+1] - cu_seqlens_k[b].  A position
+// before the sequence start or on a page id outside the pool is not written.
+int oracle_write_new_kv(const uint16_t* k_new, const uint16_t* v_new, int32_t num_seqs,
+                        const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, const oracle_kv* kv,
+                        float k_descale, float v_descale) {
+  if (!k_new || !v_new || !cu_seqlens_q || !cu_seqlens_k || !kv || kv->dtype != kFP8) return 1;
+  uint8_t* kp = static_cast<uint8_t*>(const_cast<void*>(kv->k_cache));
+  uint8_t* vp = static_cast<uint8_t*>(const_cast<void*>(kv->v_cache));
+  const int hkv = kv->num_kv_heads;
+  for (int b = 0; b < num_seqs; ++b) {
+    const int64_t lq = cu_seqlens_q[b + 1] - cu_seqlens_q[b];
+    const int64_t lk = cu_seqlens_k[b + 1] - cu_seqlens_k[b];
+    for (int64_t t = 0; t < lq; ++t) {
+      const int64_t pos = lk - lq + t;
+      if (pos < 0) continue;
+      const int64_t tok = cu_seqlens_q[b] + t;
+      for (int g = 0; g < hkv; ++g) {
+        const int64_t ko = key_offset(*kv, b, pos, g, false);
+        const int64_t vo = key_offset(*kv, b, pos, g, true);
+        const int64_t src = (tok * hkv + g) * kHeadDim;
+        for (int d = 0; d < kHeadDim; ++d) {
+          if (ko >= 0) kp[ko + d] = quantize_one(k_new[src + d], k_descale);
+          if (vo >= 0) vp[vo + d] = quantize_one(v_new[src + d], v_descale);
+        }
+      }
+    }
+  }
+  return 0;
+}
+
+}  // extern "C"

@@ -6,6 +6,6 @@ the fp64 oracle and the HIP library can consume the same inputs without
 sharing any code path.
 """
 from .synth import (  # noqa: F401
-    Problem, BF16, FP8, NAN_CODE, config, config_names, make_causal, make_sparse,
+    Problem, BF16, FP8, NAN_CODE, config, config_names, make_causal, make_sparse, make_prefill_quant,
     poison_unused, visible_pairs, kv_bytes_read, gathered_bytes, sample_rows,
 )

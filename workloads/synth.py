@@ -290,6 +290,43 @@ def make_sparse(name, seed, lens_q, lens_k, num_q_heads, num_kv_heads, num_selec
                    indices=idx, meta={"seed": seed})
 
 
+def make_prefill_quant(name, seed, lens_q, lens_k, num_q_heads, num_kv_heads, *, page_size=16, layout="NHD",
+                       q_sigma=1.0, kv_sigma=1.0, pool_pages=None) -> Problem:
+    """Prefix-hit prefill inputs as they stand before the casts to FP8.
+
+    The cached prefix sits in an FP8 pool under static per-tensor descales; Q
+    and the new tokens' keys and values are bf16: ``p.q`` holds Q's bf16
+    patterns, ``meta['k_new']`` / ``meta['v_new']`` the new keys and values
+    ``[T, Hkv, 256]`` (token order of cu_seqlens_q) and ``meta['cu_seqlens_k']``
+    the cumulative key lengths.  The pool slots of the new positions hold NaN
+    codes until something writes them.
+    """
+    p = make_causal(name, seed, lens_q, lens_k, num_q_heads, num_kv_heads, kv_dtype=FP8, q_dtype=BF16,
+                    page_size=page_size, pool_pages=pool_pages, kv_sigma=kv_sigma, q_sigma=q_sigma,
+                    layout=layout, mode="prefill")
+    s_kn, s_vn = np.random.SeedSequence(list(np.atleast_1d(seed)) + [7]).spawn(2)
+    T = p.num_tokens
+    n = T * num_kv_heads * HEAD_DIM
+    p.meta["k_new"] = _to_bf16_bits(_normal(s_kn, n, kv_sigma)).reshape(T, num_kv_heads, HEAD_DIM)
+    p.meta["v_new"] = _to_bf16_bits(_normal(s_vn, n, kv_sigma)).reshape(T, num_kv_heads, HEAD_DIM)
+    cu_k = np.zeros(p.num_seqs + 1, dtype=np.int32)
+    cu_k[1:] = np.cumsum(p.seq_lens_k)
+    p.meta["cu_seqlens_k"] = cu_k
+    nan = NAN_CODE[FP8]
+    for b in range(p.num_seqs):
+        lq = int(p.cu_seqlens_q[b + 1] - p.cu_seqlens_q[b])
+        lk = int(p.seq_lens_k[b])
+        pos = np.arange(lk - lq, lk)
+        pages, slots = p.block_table[b, pos // page_size], pos % page_size
+        if layout == "NHD":
+            p.k_cache[pages, slots] = nan
+            p.v_cache[pages, slots] = nan
+        else:
+            p.k_cache[pages, :, slots] = nan
+            p.v_cache[pages, :, slots] = nan
+    return p
+
+
 # ---------------------------------------------------------------------------
 # The five named workloads.
 # ---------------------------------------------------------------------------
@@ -302,6 +339,7 @@ _CONFIGS = {
     "sparse_bf16": 5,
     "sparse_fp8": 5,
     "sparse_fp8_260rows": 6,
+    "prefill_quant_32k": 7,
 }
 
 
@@ -336,6 +374,10 @@ def config(name: str) -> Problem:
         sub = 0 if name.endswith("32k") else 1
         return make_causal(name, [c, sub], [16384], [lk], 8, 1, kv_dtype=FP8, q_dtype=FP8,
                            mode="prefill")
+    if name == "prefill_quant_32k":
+        # The 16k-new / 32k-context prefill before its casts to FP8: bf16 Q and
+        # new K/V, the 16384-token prefix already in the FP8 pool.
+        return make_prefill_quant(name, [c, 0], [16384], [32768], 8, 1)
     if name == "sparse_fp8_260rows":
         # The few-row regime of the same selection: the last 260 rows of the
         # 32768-token sequence, 24 q / 2 kv, 2051 selected tokens each, FP8 K/V.
