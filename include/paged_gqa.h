@@ -2,7 +2,7 @@
  * paged_gqa.h -- C ABI of a gfx950 (MI355X) library for paged grouped-query
  * attention with head_dim 256 over a block-table-indexed KV cache.
  *
- * Three calls, one per problem on the source pages:
+ * Three attention calls, one per problem on the source pages:
  *   paged_attn_verify          short multi-token speculative-verify queries
  *                              (SGLang PR #36330, "... MTP unified attention on
  *                              gfx950": Motivation, Modifications)
@@ -14,8 +14,13 @@
  *                              selected tokens (vLLM PR #62590, "Tune sparse GQA
  *                              prefill profile on gfx942 and gfx950": Overview,
  *                              Earlier results)
+ * and the step ahead of the FP8 prefill:
+ *   prefill_quantize_fp8       per-tensor FP8 quantisation of Q and of the new
+ *                              tokens' keys and values into the page pool
+ *                              (ROCm/ATOM PR #2534: the casts to FP8 counted in
+ *                              its prefill timings)
  *
- * What every call computes, for sequence b, query token t (0 <= t < Lq_b) and
+ * What every attention call computes, for sequence b, query token t (0 <= t < Lq_b) and
  * query head h, with r = num_q_heads / num_kv_heads and g = h / r:
  *   s_j  = softmax_scale * q_descale * k_descale * <q[t,h,:], K_j[g,:]>
  *   out  = v_descale * sum_j softmax(s)_j * V_j[g,:]       (bf16, RNE)
@@ -60,7 +65,7 @@
 extern "C" {
 #endif
 
-#define PGA_ABI_VERSION 2
+#define PGA_ABI_VERSION 3
 #define PGA_HEAD_DIM 256
 
 /* Element encodings. */
@@ -226,6 +231,51 @@ int32_t sparse_paged_attn_splits(int32_t num_q_heads, int32_t num_kv_heads, int3
                                  int32_t num_selected);
 size_t sparse_paged_attn_workspace_bytes(int32_t num_q_heads, int32_t num_kv_heads, int32_t num_q_tokens,
                                          int32_t num_selected);
+
+/*
+ * Per-tensor FP8 (OCP E4M3FN) quantisation of a prefix-hit prefill's inputs,
+ * the step ahead of paged_attn_prefill_prefix with FP8 Q (ROCm/ATOM PR #2534,
+ * FMHA commit message and Results: its prefill timings include the casts of
+ * Q, K and V to FP8).  The page fixes no scale rule; this call takes the
+ * plainest one, in fp32:
+ *   descale = fp32(amax / 448), amax = max |x| over the non-NaN elements
+ *             (descale 1 when amax is 0)
+ *   code    = the E4M3FN value nearest to fp32(x / descale), ties to the even
+ *             code; finite values beyond +-448 saturate to +-448, NaN stays NaN
+ * Q takes a dynamic descale (or a given one); the new tokens' keys and values
+ * take the pool's own descales (kv->k_descale, kv->v_descale; NULL = 1), which
+ * the cached prefix in the pool already uses, and are written into the pool
+ * at logical position Lk_b - Lq_b + t of their sequence.
+ *
+ *   q             [num_q_tokens, num_q_heads, 256] bf16, 16-byte aligned
+ *                 (q and q_fp8 may be NULL when num_q_tokens is 0)
+ *   q_descale_in  device scalar with the descale to use, or NULL for the
+ *                 dynamic one
+ *   q_fp8         [num_q_tokens, num_q_heads, 256] codes out, 8-byte aligned
+ *   q_descale_out device scalar out: the descale used (pass it as q_descale to
+ *                 paged_attn_prefill_prefix); may be NULL when q_descale_in is set
+ *   k_new, v_new  [num_q_tokens, kv->num_kv_heads, 256] bf16 in the token
+ *                 order of cu_seqlens_q, 16-byte aligned; both NULL for Q only
+ *   cu_seqlens_q, cu_seqlens_k  [num_seqs + 1] int32 prefix sums of Lq_b and
+ *                 Lk_b (needed with k_new / v_new)
+ *   kv            the FP8 pool (required with k_new / v_new).  The call WRITES
+ *                 the new tokens' rows into kv->k_cache and kv->v_cache; other
+ *                 slots are untouched.  A position before its sequence's start
+ *                 or on a page id outside [0, num_pages) is not written.
+ *   workspace     with the dynamic descale: a device buffer of at least
+ *                 prefill_quantize_fp8_workspace_bytes() bytes, 256-byte
+ *                 aligned (per-workgroup maxima); otherwise unused
+ * Two launches with the dynamic descale (a max-magnitude reduction over Q,
+ * then the coding pass), one with a given descale.  Returns PGA_OK or a
+ * PGA_ERR_* code.
+ */
+int prefill_quantize_fp8(const void* q, int32_t num_q_heads, int32_t num_q_tokens, const float* q_descale_in,
+                         void* q_fp8, float* q_descale_out, const void* k_new, const void* v_new, int32_t num_seqs,
+                         const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, const pga_paged_kv* kv,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes prefill_quantize_fp8 needs with the dynamic descale. */
+size_t prefill_quantize_fp8_workspace_bytes(void);
 
 /* Human-readable text of a status code (static storage). */
 const char* pga_status_string(int status);

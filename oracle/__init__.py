@@ -187,3 +187,19 @@ def write_new_kv(p, k_new: np.ndarray, v_new: np.ndarray, cu_seqlens_k: np.ndarr
     if rc != 0:
         raise ValueError("oracle rejected the key/value write (code %d)" % rc)
 
+
+def quantized_problem(p):
+    """The oracle's FP8 quantisation of a quantising prefill problem (one whose
+    ``meta`` holds bf16 ``k_new`` / ``v_new``): a copy whose Q holds the FP8
+    codes under the dynamic descale and whose pool holds the new keys and
+    values, ready for :func:`attention`."""
+    import copy
+
+    r = copy.copy(p)
+    r.k_cache, r.v_cache = p.k_cache.copy(), p.v_cache.copy()
+    r.q, r.q_descale = quantize_fp8(p.q)
+    r.q_dtype = "fp8_e4m3"
+    write_new_kv(r, p.meta["k_new"], p.meta["v_new"], p.meta["cu_seqlens_k"])
+    r.meta = {k: v for k, v in p.meta.items() if k not in ("k_new", "v_new")}
+    return r
+

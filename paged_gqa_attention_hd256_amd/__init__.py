@@ -20,7 +20,7 @@ import torch
 
 __all__ = [
     "PagedKV", "paged_attn_verify", "paged_attn_prefill_prefix", "sparse_paged_attn", "sparse_splits",
-    "sparse_workspace_bytes",
+    "sparse_workspace_bytes", "prefill_quantize_fp8", "quantize_workspace_bytes",
     "verify_workspace_bytes", "verify_split_tokens", "status_string", "abi_version", "library_path",
     "PagedGQAError", "LibraryNotBuilt", "load_library",
 ]
@@ -87,6 +87,10 @@ def load_library():
             lib.sparse_paged_attn_splits.restype = I32
             lib.sparse_paged_attn_workspace_bytes.argtypes = [I32, I32, I32, I32]
             lib.sparse_paged_attn_workspace_bytes.restype = SZ
+            lib.prefill_quantize_fp8.argtypes = [P, I32, I32, P, P, P, P, P, I32, P, P, ctypes.c_void_p, P, SZ, P]
+            lib.prefill_quantize_fp8.restype = ctypes.c_int
+            lib.prefill_quantize_fp8_workspace_bytes.argtypes = []
+            lib.prefill_quantize_fp8_workspace_bytes.restype = SZ
             lib.pga_status_string.argtypes = [ctypes.c_int]
             lib.pga_status_string.restype = ctypes.c_char_p
             lib.pga_abi_version.argtypes = []
@@ -267,3 +271,39 @@ def sparse_paged_attn(q, cu_seqlens_q, seq_lens_k, indices, kv: PagedKV, softmax
                                out.data_ptr(), _ptr(lse), _stream(stream))
     _check("sparse_paged_attn", st)
     return out
+
+
+def quantize_workspace_bytes() -> int:
+    return load_library().prefill_quantize_fp8_workspace_bytes()
+
+
+def prefill_quantize_fp8(q, kv: Optional[PagedKV] = None, k_new=None, v_new=None, cu_seqlens_q=None,
+                         cu_seqlens_k=None, q_descale=None, q_fp8=None, q_descale_out=None, workspace=None,
+                         stream=None):
+    """Per-tensor FP8 quantisation ahead of the FP8 prefill.  Codes bf16 ``q``
+    ([T, Hq, 256]) into ``q_fp8`` (float8_e4m3fn) with the descale ``q_descale``
+    (a 1-element fp32 tensor) or, when that is None, the dynamic descale
+    amax/448, which lands in ``q_descale_out``; with ``k_new``/``v_new``
+    ([T, Hkv, 256] bf16) it also writes the new tokens' keys and values into
+    ``kv``'s FP8 pool under the pool's descales.  Returns (q_fp8, q_descale_out)."""
+    lib = load_library()
+    if q.dtype != torch.bfloat16 or q.dim() != 3 or not q.is_contiguous():
+        raise ValueError("q must be a contiguous bf16 [T, Hq, 256] tensor")
+    if q_fp8 is None:
+        q_fp8 = torch.empty(q.shape, dtype=torch.float8_e4m3fn, device=q.device)
+    if q_descale_out is None:
+        q_descale_out = torch.empty(1, dtype=torch.float32, device=q.device)
+    if q_descale is None and workspace is None:
+        workspace = torch.empty(quantize_workspace_bytes(), dtype=torch.uint8, device=q.device)
+    s = kv._struct() if kv is not None else None
+    for t in (k_new, v_new):
+        if t is not None and (t.dtype != torch.bfloat16 or not t.is_contiguous()):
+            raise ValueError("k_new / v_new must be contiguous bf16 [T, Hkv, 256] tensors")
+    num_seqs = cu_seqlens_q.shape[0] - 1 if cu_seqlens_q is not None else 0
+    st = lib.prefill_quantize_fp8(q.data_ptr(), q.shape[1], q.shape[0], _ptr(q_descale), q_fp8.data_ptr(),
+                                  q_descale_out.data_ptr(), _ptr(k_new), _ptr(v_new), num_seqs, _ptr(cu_seqlens_q),
+                                  _ptr(cu_seqlens_k), None if s is None else ctypes.addressof(s), _ptr(workspace),
+                                  0 if workspace is None else workspace.numel() * workspace.element_size(),
+                                  _stream(stream))
+    _check("prefill_quantize_fp8", st)
+    return q_fp8, q_descale_out

@@ -396,4 +396,52 @@ int32_t sparse_paged_attn_splits(int32_t num_q_heads, int32_t num_kv_heads, int3
   return plan_sparse(num_q_heads, num_kv_heads, num_q_tokens, num_selected, p) ? p.splits : 0;
 }
 
+size_t prefill_quantize_fp8_workspace_bytes(void) { return pga::kQuantMaxPartials * sizeof(uint32_t); }
+
+int prefill_quantize_fp8(const void* q, int32_t num_q_heads, int32_t num_q_tokens, const float* q_descale_in,
+                         void* q_fp8, float* q_descale_out, const void* k_new, const void* v_new, int32_t num_seqs,
+                         const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, const pga_paged_kv* kv,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  if ((!q || !q_fp8) && num_q_tokens > 0) return PGA_ERR_NULL;
+  if (!q_descale_in && !q_descale_out) return PGA_ERR_NULL;
+  if (!k_new != !v_new) return PGA_ERR_NULL;
+  if (num_q_heads <= 0 || num_q_tokens < 0 || num_seqs < 0) return PGA_ERR_SHAPE;
+  if (!aligned(q, 16) || !aligned(q_fp8, 8) || (q_descale_out && !aligned(q_descale_out, 4)))
+    return PGA_ERR_UNSUPPORTED;
+  const bool with_kv = k_new != nullptr;
+  if (with_kv) {
+    if (!cu_seqlens_q || !cu_seqlens_k || !kv) return PGA_ERR_NULL;
+    if (int e = check_kv(kv, num_q_heads, -1)) return e;
+    if (kv->dtype != kFP8) return PGA_ERR_DTYPE;
+    if (num_q_tokens > 0 && num_seqs == 0) return PGA_ERR_SHAPE;
+    if (!aligned(k_new, 16) || !aligned(v_new, 16)) return PGA_ERR_UNSUPPORTED;
+    if (int64_t(num_q_tokens) * kv->num_kv_heads * (kHeadDim / 8) > INT32_MAX) return PGA_ERR_UNSUPPORTED;
+  }
+  const bool dynamic = q_descale_in == nullptr;
+  if (dynamic) {
+    if (!workspace || workspace_bytes < prefill_quantize_fp8_workspace_bytes()) return PGA_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return PGA_ERR_UNSUPPORTED;
+  }
+
+  pga::QuantArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.q_chunks = int64_t(num_q_tokens) * num_q_heads * (kHeadDim / 8);
+  a.q_ds_in = q_descale_in;
+  a.q_ds_out = q_descale_out;
+  a.q_out = static_cast<uint8_t*>(q_fp8);
+  a.partial = static_cast<uint32_t*>(workspace);
+  a.num_partial = dynamic ? pga::quant_amax_blocks(a.q_chunks) : 0;
+  if (with_kv) {
+    a.k_new = static_cast<const uint16_t*>(k_new);
+    a.v_new = static_cast<const uint16_t*>(v_new);
+    a.kv_rows = int64_t(num_q_tokens) * kv->num_kv_heads;
+    a.num_seqs = num_seqs;
+    a.cu_q = cu_seqlens_q;
+    a.cu_k = cu_seqlens_k;
+    a.kv = make_kv(kv);
+  }
+  a.max_blocks = int64_t(device_cus()) * 8;
+  return launch_status(pga::launch_quantize(a, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -81,6 +81,26 @@ struct SparseArgs {
   float* ws_lse;           // [T * hq * splits] natural-log lse of the pieces
 };
 
+// FP8 quantisation of a prefill's inputs (quantize.hip).
+constexpr int kQuantMaxPartials = 1024;  // partial maxima of the reduction pass
+struct QuantArgs {
+  const uint16_t* q;       // [T, hq, 256] bf16
+  int64_t q_chunks;        // 16-byte chunks of q: T * hq * 32
+  const float* q_ds_in;    // given descale, or null for the dynamic one (amax / 448)
+  float* q_ds_out;         // the descale used, or null
+  uint8_t* q_out;          // [T, hq, 256] E4M3FN codes
+  uint32_t* partial;       // [num_partial] per-workgroup max |q| as bf16 magnitude patterns
+  int32_t num_partial;
+  const uint16_t* k_new;   // [T, hkv, 256] bf16, or null (then kv_rows is 0)
+  const uint16_t* v_new;
+  int64_t kv_rows;         // T * hkv
+  int32_t num_seqs;
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  KvArgs kv;               // the FP8 pool the new keys and values are written into
+  int64_t max_blocks;      // grid cap of the coding pass
+};
+
 // Launchers (defined next to their kernels).  They return the launch status.
 hipError_t launch_verify(const VerifyArgs& a, int kv_dtype, int num_wg, hipStream_t s);
 hipError_t launch_verify_merge(const VerifyArgs& a, int kv_dtype, int num_wg, hipStream_t s);
@@ -88,5 +108,8 @@ hipError_t launch_verify_merge(const VerifyArgs& a, int kv_dtype, int num_wg, hi
 int prefill_tile_tokens(int q_dtype, int kv_dtype, int r);
 hipError_t launch_prefill(const PrefillArgs& a, int q_dtype, int kv_dtype, int q_tiles, hipStream_t s);
 hipError_t launch_sparse(const SparseArgs& a, int kv_dtype, hipStream_t s);
+// Workgroups of the reduction pass for q_chunks 16-byte chunks (1 .. kQuantMaxPartials).
+int quant_amax_blocks(int64_t q_chunks);
+hipError_t launch_quantize(const QuantArgs& a, hipStream_t s);
 
 }  // namespace pga

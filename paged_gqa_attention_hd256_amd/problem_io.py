@@ -4,8 +4,10 @@
 problem (numpy arrays of raw bf16 / FP8 codes: ``q``, ``k_cache``,
 ``v_cache``, ``block_table``, ``cu_seqlens_q``, ``seq_lens_k``, optional
 ``indices``; scalars ``q_dtype``, ``kv_dtype``, descales, ``softmax_scale``,
-``mode``, ``kv_layout``, ``kv_split_tokens``).  It only moves data; the
-attention itself runs in the HIP library.
+``mode``, ``kv_layout``, ``kv_split_tokens``).  A prefill problem whose
+``meta`` carries bf16 ``k_new`` / ``v_new`` (and ``q`` in bf16) runs as the
+FP8 quantisation of Q and the new keys/values followed by the FP8 prefill.
+It only moves data; the computation itself runs in the HIP library.
 """
 from __future__ import annotations
 
@@ -15,8 +17,8 @@ from typing import Optional
 import numpy as np
 import torch
 
-from . import (PagedKV, paged_attn_prefill_prefix, paged_attn_verify, sparse_paged_attn, sparse_workspace_bytes,
-               verify_workspace_bytes)
+from . import (PagedKV, paged_attn_prefill_prefix, paged_attn_verify, prefill_quantize_fp8, quantize_workspace_bytes,
+               sparse_paged_attn, sparse_workspace_bytes, verify_workspace_bytes)
 
 
 def _codes_to_tensor(codes: np.ndarray, dtype: str, device) -> torch.Tensor:
@@ -30,6 +32,18 @@ def _codes_to_tensor(codes: np.ndarray, dtype: str, device) -> torch.Tensor:
 
 def _scalar(x: float, device) -> torch.Tensor:
     return torch.tensor([x], dtype=torch.float32, device=device)
+
+
+@dataclass
+class QuantBuffers:
+    """Inputs and outputs of the FP8 quantisation ahead of a prefill."""
+
+    q_bf16: torch.Tensor
+    k_new: torch.Tensor
+    v_new: torch.Tensor
+    q_fp8: torch.Tensor
+    q_descale: torch.Tensor
+    workspace: torch.Tensor
 
 
 @dataclass
@@ -49,6 +63,7 @@ class DeviceProblem:
     out: torch.Tensor
     lse: torch.Tensor
     workspace: Optional[torch.Tensor]
+    quant: Optional[QuantBuffers] = None
 
 
 def to_device(p, device="cuda", kv_split_tokens: Optional[int] = None) -> DeviceProblem:
@@ -82,8 +97,25 @@ def to_device(p, device="cuda", kv_split_tokens: Optional[int] = None) -> Device
         if need:
             ws = torch.empty(need, dtype=torch.uint8, device=device)
     q_ds = _scalar(p.q_descale, device) if p.q_dtype != "bf16" else None
+    quant = None
+    meta = getattr(p, "meta", None) or {}
+    if p.mode == "prefill" and "k_new" in meta:
+        quant = QuantBuffers(q, _codes_to_tensor(meta["k_new"], "bf16", device),
+                             _codes_to_tensor(meta["v_new"], "bf16", device),
+                             torch.empty(q.shape, dtype=torch.float8_e4m3fn, device=device),
+                             torch.empty(1, dtype=torch.float32, device=device),
+                             torch.empty(quantize_workspace_bytes(), dtype=torch.uint8, device=device))
     return DeviceProblem(p.mode, q, q_ds, cu_q, lens_k, cu_k, kv, float(p.softmax_scale), max_q, max_k, split, idx,
-                         out, lse, ws)
+                         out, lse, ws, quant)
+
+
+def quantize(dp: DeviceProblem, stream=None):
+    """The FP8 quantisation of a quantising prefill problem: Q into
+    ``dp.quant.q_fp8`` (dynamic descale into ``dp.quant.q_descale``), the new
+    keys and values into the pool."""
+    qb = dp.quant
+    return prefill_quantize_fp8(qb.q_bf16, dp.kv, qb.k_new, qb.v_new, dp.cu_seqlens_q, dp.cu_seqlens_k,
+                                q_fp8=qb.q_fp8, q_descale_out=qb.q_descale, workspace=qb.workspace, stream=stream)
 
 
 def run(dp: DeviceProblem, stream=None, stage: str = "all") -> torch.Tensor:
@@ -94,6 +126,15 @@ def run(dp: DeviceProblem, stream=None, stage: str = "all") -> torch.Tensor:
         return paged_attn_verify(dp.q, dp.cu_seqlens_q, dp.seq_lens_k, dp.max_q_len, dp.max_kv_len, dp.kv,
                                  dp.softmax_scale, dp.kv_split_tokens, q_descale=dp.q_descale, workspace=dp.workspace,
                                  out=dp.out, lse=dp.lse, stream=stream, stage=stage)
+    if dp.mode == "prefill" and dp.quant is not None:
+        # stage "all": quantise, then attend; "quant" / "attn": one of the two
+        if stage in ("all", "quant"):
+            quantize(dp, stream)
+        if stage == "quant":
+            return dp.quant.q_fp8
+        return paged_attn_prefill_prefix(dp.quant.q_fp8, dp.cu_seqlens_q, dp.cu_seqlens_k, dp.max_q_len,
+                                         dp.max_kv_len, dp.kv, dp.softmax_scale, q_descale=dp.quant.q_descale,
+                                         out=dp.out, lse=dp.lse, stream=stream)
     if dp.mode == "prefill":
         return paged_attn_prefill_prefix(dp.q, dp.cu_seqlens_q, dp.cu_seqlens_k, dp.max_q_len, dp.max_kv_len, dp.kv,
                                          dp.softmax_scale, q_descale=dp.q_descale, out=dp.out, lse=dp.lse,

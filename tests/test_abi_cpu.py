@@ -36,7 +36,7 @@ def test_library_exports_every_declared_function(lib):
     assert {"paged_attn_verify", "paged_attn_prefill_prefix", "sparse_paged_attn"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.pga_abi_version() == 2
+    assert lib.pga_abi_version() == 3
 
 
 def test_status_strings(lib):
@@ -201,3 +201,32 @@ def test_sparse_split_plan(lib):
     assert lib.sparse_paged_attn_splits(24, 2, 8, 2048) == 8
     assert lib.sparse_paged_attn_splits(24, 2, 8192, 2051) == 1      # the large-row workload: no split
     assert lib.sparse_paged_attn_splits(25, 2, 8, 64) == 0          # invalid head counts
+
+
+def quantize(lib, kv=None, **kw):
+    a = dict(q=P(), hq=8, ntok=16, qds=None, qfp8=P(20000), qds_out=P(40000), k_new=P(24576), v_new=P(28672),
+             nseq=1, cuq=P(16384), cuk=P(16384 + 64), ws=P(1 << 15), wsb=4096)
+    a.update(kw)
+    kv = kv or kv_struct()
+    return lib.prefill_quantize_fp8(a["q"], a["hq"], a["ntok"], a["qds"], a["qfp8"], a["qds_out"], a["k_new"],
+                                    a["v_new"], a["nseq"], a["cuq"], a["cuk"], ctypes.addressof(kv), a["ws"],
+                                    a["wsb"], None)
+
+
+def test_quantize_rejects_invalid_arguments(lib):
+    assert lib.prefill_quantize_fp8_workspace_bytes() == 4096
+    assert quantize(lib, q=None) == ENULL
+    assert quantize(lib, qfp8=None) == ENULL
+    assert quantize(lib, qds_out=None) == ENULL                # the dynamic descale needs somewhere to go
+    assert quantize(lib, v_new=None) == ENULL                 # keys without values
+    assert quantize(lib, cuk=None) == ENULL
+    assert quantize(lib, hq=0) == ESHAPE
+    assert quantize(lib, ntok=-1) == ESHAPE
+    assert quantize(lib, nseq=0) == ESHAPE                    # new tokens without a sequence
+    assert quantize(lib, kv=kv_struct(num_kv_heads=5)) == ESHAPE
+    assert quantize(lib, kv=kv_struct(dtype=1)) == EDTYPE     # the pool must be FP8
+    assert quantize(lib, q=P(8)) == EUNSUP                    # q not 16-byte aligned
+    assert quantize(lib, k_new=P(24584)) == EUNSUP
+    assert quantize(lib, wsb=4095) == EWS
+    assert quantize(lib, ws=None) == EWS
+    assert quantize(lib, ws=P((1 << 15) + 16)) == EUNSUP      # workspace not 256-byte aligned
