@@ -82,7 +82,8 @@ enum pga_status {
   PGA_ERR_DTYPE = 3,       /* unsupported dtype or q/kv dtype pair */
   PGA_ERR_UNSUPPORTED = 4, /* outside the kernel envelope: page size, alignment, rows per group */
   PGA_ERR_WORKSPACE = 5,   /* workspace smaller than the matching *_workspace_bytes() */
-  PGA_ERR_LAUNCH = 6       /* the HIP runtime refused a launch */
+  PGA_ERR_LAUNCH = 6,      /* the HIP runtime refused a launch (or a copy / synchronisation failed) */
+  PGA_ERR_INVALID_DATA = 7 /* pga_validate_inputs found device data that breaks a precondition */
 };
 
 /* The paged KV cache.  K and V share dtype, head count and page size; their
@@ -276,6 +277,43 @@ int prefill_quantize_fp8(const void* q, int32_t num_q_heads, int32_t num_q_token
 
 /* Workspace bytes prefill_quantize_fp8 needs with the dynamic descale. */
 size_t prefill_quantize_fp8_workspace_bytes(void);
+
+/*
+ * Checks the data-dependent preconditions that the calls above leave
+ * unchecked because checking them would need a synchronisation (the survey of
+ * the pages' dispatch gates in SGLang PR #36330, review notes, is the reason
+ * the library never guesses silently instead).  For tests and debugging, not
+ * for the hot path: it launches small kernels on `stream` and then
+ * synchronises the stream.  Every device read stays inside the extents the
+ * host arguments give, whatever the device data hold.
+ *
+ *   num_seqs, cu_seqlens_q  as in the attention calls
+ *   num_q_tokens  host copy of cu_seqlens_q[num_seqs], or -1 when unknown
+ *                 (required, >= 0, with indices)
+ *   seq_lens_k, cu_seqlens_k  exactly one of them (verify and sparse take
+ *                 seq_lens_k, prefill cu_seqlens_k)
+ *   max_q_len, max_kv_len  the host bounds the caller passes to the call
+ *                 (<= 0: not checked)
+ *   kv            the pool: block_table, block_table_stride, page_size and
+ *                 num_pages are read
+ *   indices, index_stride, num_selected  sparse lists, or indices NULL
+ *   counts_device device int32[4] scratch, overwritten
+ *   counts_host   host int32[4] out, or NULL:
+ *     [0] sequences with invalid lengths (cu_seqlens_q not starting at 0 or
+ *         decreasing, Lk_b < Lq_b, cu_seqlens_q[num_seqs] != num_q_tokens)
+ *     [1] sequences beyond the host bounds, or needing more block-table
+ *         columns than block_table_stride
+ *     [2] block-table entries, among those the keys 0 .. Lk_b - 1 map to,
+ *         outside [0, num_pages)
+ *     [3] index entries at or past their sequence's Lk_b (the sparse call
+ *         skips them like padding; reported, not an error)
+ * Returns PGA_OK when counts [0] .. [2] are zero, PGA_ERR_INVALID_DATA when
+ * not, or another PGA_ERR_* code for invalid host arguments.
+ */
+int pga_validate_inputs(int32_t num_seqs, int32_t num_q_tokens, const int32_t* cu_seqlens_q,
+                        const int32_t* seq_lens_k, const int32_t* cu_seqlens_k, int32_t max_q_len,
+                        int32_t max_kv_len, const pga_paged_kv* kv, const int32_t* indices, int64_t index_stride,
+                        int32_t num_selected, int32_t* counts_device, int32_t* counts_host, void* stream);
 
 /* Human-readable text of a status code (static storage). */
 const char* pga_status_string(int status);

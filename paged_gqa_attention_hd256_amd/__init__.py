@@ -20,7 +20,7 @@ import torch
 
 __all__ = [
     "PagedKV", "paged_attn_verify", "paged_attn_prefill_prefix", "sparse_paged_attn", "sparse_splits",
-    "sparse_workspace_bytes", "prefill_quantize_fp8", "quantize_workspace_bytes",
+    "sparse_workspace_bytes", "prefill_quantize_fp8", "quantize_workspace_bytes", "validate_inputs",
     "verify_workspace_bytes", "verify_split_tokens", "status_string", "abi_version", "library_path",
     "PagedGQAError", "LibraryNotBuilt", "load_library",
 ]
@@ -91,6 +91,8 @@ def load_library():
             lib.prefill_quantize_fp8.restype = ctypes.c_int
             lib.prefill_quantize_fp8_workspace_bytes.argtypes = []
             lib.prefill_quantize_fp8_workspace_bytes.restype = SZ
+            lib.pga_validate_inputs.argtypes = [I32, I32, P, P, P, I32, I32, KVP, P, I64, I32, P, P, P]
+            lib.pga_validate_inputs.restype = ctypes.c_int
             lib.pga_status_string.argtypes = [ctypes.c_int]
             lib.pga_status_string.restype = ctypes.c_char_p
             lib.pga_abi_version.argtypes = []
@@ -307,3 +309,29 @@ def prefill_quantize_fp8(q, kv: Optional[PagedKV] = None, k_new=None, v_new=None
                                   _stream(stream))
     _check("prefill_quantize_fp8", st)
     return q_fp8, q_descale_out
+
+
+def validate_inputs(cu_seqlens_q, kv: PagedKV, seq_lens_k=None, cu_seqlens_k=None, max_q_len: int = 0,
+                    max_kv_len: int = 0, indices=None, num_selected: Optional[int] = None, stream=None):
+    """Check the device data the attention calls take on trust (lengths, block
+    table, index lists); synchronous.  Returns (status, counts) with counts =
+    [invalid-length sequences, sequences beyond the bounds, bad block-table
+    entries, index entries past Lk]; status is 0 or PGA_ERR_INVALID_DATA (7)."""
+    lib = load_library()
+    s = kv._struct()
+    counts = torch.empty(4, dtype=torch.int32, device=cu_seqlens_q.device)
+    host = (ctypes.c_int32 * 4)()
+    num_seqs = cu_seqlens_q.shape[0] - 1
+    ntok = -1
+    stride, ns = 0, 0
+    if indices is not None:
+        if indices.dtype != torch.int32 or indices.dim() != 2 or indices.stride(1) != 1:
+            raise ValueError("indices must be a row-major int32 [T, W] tensor")
+        ntok, stride = indices.shape[0], indices.stride(0)
+        ns = indices.shape[1] if num_selected is None else num_selected
+    st = lib.pga_validate_inputs(num_seqs, ntok, cu_seqlens_q.data_ptr(), _ptr(seq_lens_k), _ptr(cu_seqlens_k),
+                                 max_q_len, max_kv_len, ctypes.byref(s), _ptr(indices), stride, ns,
+                                 counts.data_ptr(), host, _stream(stream))
+    if st not in (OK, 7):
+        _check("pga_validate_inputs", st)
+    return st, list(host)

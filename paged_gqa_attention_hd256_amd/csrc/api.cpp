@@ -176,6 +176,7 @@ const char* pga_status_string(int status) {
     case PGA_ERR_UNSUPPORTED: return "outside the kernel envelope (page size, alignment, rows per kv group)";
     case PGA_ERR_WORKSPACE: return "workspace too small";
     case PGA_ERR_LAUNCH: return "kernel launch failed";
+    case PGA_ERR_INVALID_DATA: return "device data break a precondition (see the counts)";
     default: return "unknown status";
   }
 }
@@ -442,6 +443,42 @@ int prefill_quantize_fp8(const void* q, int32_t num_q_heads, int32_t num_q_token
   }
   a.max_blocks = int64_t(device_cus()) * 8;
   return launch_status(pga::launch_quantize(a, static_cast<hipStream_t>(stream)));
+}
+
+int pga_validate_inputs(int32_t num_seqs, int32_t num_q_tokens, const int32_t* cu_seqlens_q,
+                        const int32_t* seq_lens_k, const int32_t* cu_seqlens_k, int32_t max_q_len,
+                        int32_t max_kv_len, const pga_paged_kv* kv, const int32_t* indices, int64_t index_stride,
+                        int32_t num_selected, int32_t* counts_device, int32_t* counts_host, void* stream) {
+  if (!cu_seqlens_q || !kv || !kv->block_table || !counts_device) return PGA_ERR_NULL;
+  if (!seq_lens_k == !cu_seqlens_k) return PGA_ERR_NULL;  // exactly one of them
+  if (num_seqs < 0) return PGA_ERR_SHAPE;
+  if (!pow2(kv->page_size) || kv->num_pages <= 0 || kv->block_table_stride < 0) return PGA_ERR_SHAPE;
+  if (indices && (num_q_tokens < 0 || num_selected < 0 || index_stride < num_selected)) return PGA_ERR_SHAPE;
+  if (!aligned(counts_device, 4)) return PGA_ERR_UNSUPPORTED;
+  pga::ValidateArgs a{};
+  a.num_seqs = num_seqs;
+  a.num_q_tokens = num_q_tokens;
+  a.cu_q = cu_seqlens_q;
+  a.lens_k = seq_lens_k;
+  a.cu_k = cu_seqlens_k;
+  a.max_q_len = max_q_len;
+  a.max_kv_len = max_kv_len;
+  a.bt = kv->block_table;
+  a.bt_stride = kv->block_table_stride;
+  a.page_size = kv->page_size;
+  a.num_pages = kv->num_pages;
+  a.idx = indices;
+  a.idx_stride = index_stride;
+  a.num_selected = num_selected;
+  a.counts = counts_device;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (int e = launch_status(pga::launch_validate(a, s))) return e;
+  int32_t c[pga::kValidateCounts] = {0, 0, 0, 0};
+  if (hipMemcpyAsync(c, counts_device, sizeof c, hipMemcpyDeviceToHost, s) != hipSuccess) return PGA_ERR_LAUNCH;
+  if (hipStreamSynchronize(s) != hipSuccess) return PGA_ERR_LAUNCH;
+  if (counts_host)
+    for (int i = 0; i < pga::kValidateCounts; ++i) counts_host[i] = c[i];
+  return (c[0] | c[1] | c[2]) ? PGA_ERR_INVALID_DATA : PGA_OK;
 }
 
 }  // extern "C"

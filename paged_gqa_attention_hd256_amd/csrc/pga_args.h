@@ -101,6 +101,24 @@ struct QuantArgs {
   int64_t max_blocks;      // grid cap of the coding pass
 };
 
+// Device check of the data-dependent preconditions (validate.hip).
+constexpr int kValidateCounts = 4;
+struct ValidateArgs {
+  int32_t num_seqs;
+  int64_t num_q_tokens;    // host copy of cu_q[num_seqs], or -1 when unknown
+  const int32_t* cu_q;
+  const int32_t* lens_k;   // exactly one of lens_k / cu_k is set
+  const int32_t* cu_k;
+  int32_t max_q_len, max_kv_len;  // host bounds to check against (<= 0: not checked)
+  const int32_t* bt;
+  int64_t bt_stride;
+  int32_t page_size, num_pages;
+  const int32_t* idx;      // [num_q_tokens, idx_stride] or null
+  int64_t idx_stride;
+  int32_t num_selected;
+  int32_t* counts;         // [kValidateCounts] device counters
+};
+
 // Launchers (defined next to their kernels).  They return the launch status.
 hipError_t launch_verify(const VerifyArgs& a, int kv_dtype, int num_wg, hipStream_t s);
 hipError_t launch_verify_merge(const VerifyArgs& a, int kv_dtype, int num_wg, hipStream_t s);
@@ -111,5 +129,6 @@ hipError_t launch_sparse(const SparseArgs& a, int kv_dtype, hipStream_t s);
 // Workgroups of the reduction pass for q_chunks 16-byte chunks (1 .. kQuantMaxPartials).
 int quant_amax_blocks(int64_t q_chunks);
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t s);
+hipError_t launch_validate(const ValidateArgs& a, hipStream_t s);
 
 }  // namespace pga

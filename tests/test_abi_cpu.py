@@ -40,7 +40,7 @@ def test_library_exports_every_declared_function(lib):
 
 
 def test_status_strings(lib):
-    for code in range(0, 7):
+    for code in range(0, 8):
         assert pga.status_string(code)
     assert pga.status_string(99) == "unknown status"
 
@@ -230,3 +230,24 @@ def test_quantize_rejects_invalid_arguments(lib):
     assert quantize(lib, wsb=4095) == EWS
     assert quantize(lib, ws=None) == EWS
     assert quantize(lib, ws=P((1 << 15) + 16)) == EUNSUP      # workspace not 256-byte aligned
+
+
+def validate(lib, kv=None, **kw):
+    a = dict(nseq=2, ntok=8, cuq=P(16384), lk=P(16384 + 64), cuk=None, maxq=0, maxk=0, idx=None, stride=0, nsel=0,
+             counts=P(40000), host=None)
+    a.update(kw)
+    kv = kv or kv_struct()
+    return lib.pga_validate_inputs(a["nseq"], a["ntok"], a["cuq"], a["lk"], a["cuk"], a["maxq"], a["maxk"],
+                                   ctypes.byref(kv), a["idx"], a["stride"], a["nsel"], a["counts"], a["host"], None)
+
+
+def test_validate_rejects_invalid_host_arguments(lib):
+    assert validate(lib, cuq=None) == ENULL
+    assert validate(lib, lk=None) == ENULL                     # neither seq_lens_k nor cu_seqlens_k
+    assert validate(lib, cuk=P(16384 + 128)) == ENULL          # both
+    assert validate(lib, counts=None) == ENULL
+    assert validate(lib, nseq=-1) == ESHAPE
+    assert validate(lib, kv=kv_struct(page_size=24)) == ESHAPE
+    assert validate(lib, idx=P(30000), ntok=-1, stride=8, nsel=8) == ESHAPE
+    assert validate(lib, idx=P(30000), stride=4, nsel=8) == ESHAPE
+    assert validate(lib, counts=P(40002)) == EUNSUP
