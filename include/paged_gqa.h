@@ -280,10 +280,10 @@ size_t prefill_quantize_fp8_workspace_bytes(void);
 
 /*
  * Checks the data-dependent preconditions that the calls above leave
- * unchecked because checking them would need a synchronisation (the survey of
- * the pages' dispatch gates in SGLang PR #36330, review notes, is the reason
- * the library never guesses silently instead).  For tests and debugging, not
- * for the hot path: it launches small kernels on `stream` and then
+ * unchecked because checking them would need a synchronisation (SGLang PR
+ * #36330, review notes: a dispatch gate and a kernel assertion that disagree
+ * are the failure the explicit checks here and there guard against).  For
+ * tests and debugging, not for the hot path: it launches small kernels on `stream` and then
  * synchronises the stream.  Every device read stays inside the extents the
  * host arguments give, whatever the device data hold.
  *
