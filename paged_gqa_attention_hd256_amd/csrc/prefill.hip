@@ -422,12 +422,262 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_pipe_kernel(PrefillArgs a)
   }
 }
 
+// Warp-specialised schedule for FP8 Q and KV (128 rows, eight waves, one
+// workgroup per CU).  Waves 0 .. 3 compute scores and softmax, wave w for
+// rows 32 w .. 32 w + 31 (two 16-row blocks sharing every K fragment read
+// from LDS); waves 4 .. 7 compute the PV product, wave 4 + d for head dims
+// 64 d .. 64 d + 63 of all 128 rows.  Each SIMD holds one wave of each kind,
+// so the vector work of the softmax runs beside the matrix work of PV, and
+// each K tile and each tile of probabilities is read from LDS by four waves
+// instead of eight.  Iteration i: the softmax waves process tile i + 1 while
+// the PV waves multiply tile i; probabilities are double buffered, K and V
+// triple buffered as in prefill_pipe_kernel, one barrier per iteration.
+
+// Softmax of one 16-row block (rows of global block rb) on one tile, as
+// softmax_flat, also keeping the block's running row sums (all-ones A operand).
+template <bool MASKED, int NRB>
+__device__ __forceinline__ void softmax_ws(RowStat& rs, f32x4& lsum, f32x4 (&s)[4], float c2, int lim,
+                                           Exchange<kFP8, NRB>& x, int rb) {
+  const int lane = lane_id();
+  const int gq = lane >> 4, n = lane & 15;
+  float mt = kNegInf;
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if constexpr (MASKED) s[mb][i] = (mb * 16 + 4 * gq + i <= lim) ? s[mb][i] : kNegInf;
+      mt = fmaxf(mt, s[mb][i]);
+    }
+  mt = group4_max(mt);
+  mt = mt == kNegInf ? kNegInf : mt * c2;
+  const bool grow = __builtin_amdgcn_ballot_w64(mt > rs.m + kRescaleLog2) != 0;  // wave-uniform
+  const float m_new = grow ? fmaxf(rs.m, mt) : rs.m;
+  const float alpha = m_new == rs.m ? 1.f : fast_exp2(rs.m - m_new);
+  rs.m = m_new;
+  const float nm = m_new == kNegInf ? 0.f : -m_new;
+  x.row[16 * rb + n] = alpha;
+  x.grow[rb] = grow;
+  lsum *= alpha;
+  constexpr f16x8 ones = {(_Float16)1.f, (_Float16)1.f, (_Float16)1.f, (_Float16)1.f,
+                          (_Float16)1.f, (_Float16)1.f, (_Float16)1.f, (_Float16)1.f};
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    f16x8 pb;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) pb[j] = (_Float16)fast_exp2(__builtin_fmaf(s[2 * t + (j >> 2)][j & 3], c2, nm));
+    x.p[rb][t][0][lane] = __builtin_bit_cast(i32x4, pb);
+    lsum = mfma_f16(ones, pb, lsum);
+  }
+}
+
+// PV of one tile for head dims 64 d .. 64 d + 63 of all NRB row blocks, after
+// rescaling the rows whose maximum moved.
+template <int NRB>
+__device__ __forceinline__ void pv_ws(f32x4 (&o)[4 * NRB], const lds_t* vt, const Exchange<kFP8, NRB>& x, int d) {
+  using G = TileGeom<kFP8>;
+  const int lane = lane_id();
+  const int gq = lane >> 4, sl = lane & 15;
+  int any = 0;
+#pragma unroll
+  for (int i = 0; i < NRB; ++i) any |= x.grow[i];
+  // Every fragment of the tile is requested before the first product, so the
+  // LDS latency is paid once per tile rather than once per row block.
+  const int e = sl >> 1, q = sl & 1;
+  i32x2 vr[2][4];
+  i32x4 pr[2][NRB];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int key = 32 * t + 16 * (e >> 2) + 4 * gq + (e & 3);
+#pragma unroll
+    for (int db = 0; db < 4; ++db) vr[t][db] = lds_tr8(vt + G::off(key, 4 * d + db) + 8 * q);
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) pr[t][rb] = x.p[rb][t][0][lane];
+  }
+  asm volatile("" ::: "memory");
+  if (__builtin_amdgcn_readfirstlane(any) != 0) {
+#pragma unroll
+    for (int i = 0; i < 4 * NRB; ++i) asm volatile("" : "+v"(o[i]));
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) {
+      const float al = x.row[16 * rb + sl];
+#pragma unroll
+      for (int db = 0; db < 4; ++db) o[4 * rb + db] *= al;
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    f16x8 av[4];
+#pragma unroll
+    for (int db = 0; db < 4; ++db) av[db] = fp8x8_to_f16(vr[t][db]);
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) {
+      const f16x8 pb = __builtin_bit_cast(f16x8, pr[t][rb]);
+#pragma unroll
+      for (int db = 0; db < 4; ++db) o[4 * rb + db] = mfma_f16(av[db], pb, o[4 * rb + db]);
+    }
+  }
+}
+
+__global__ __launch_bounds__(512, 1) void prefill_ws_kernel(PrefillArgs a) {
+  constexpr int NW = 8, NRB = 8;
+  __shared__ PipeSmem<NRB> sm;
+  const int g = blockIdx.y, b = blockIdx.z;
+  const int tok0 = a.cu_q[b];
+  const int lq = min(a.cu_q[b + 1] - tok0, a.max_q_len);
+  const int lk = min(a.cu_k[b + 1] - a.cu_k[b], a.max_kv_len);
+  const int t_lo = (gridDim.x - 1 - blockIdx.x) * a.tile_tokens;  // longest tiles first
+  if (t_lo >= lq) return;
+  const int t_hi = min(t_lo + a.tile_tokens, lq);
+  const int k_hi = lk - lq + t_hi;
+  const int rows = a.r * (t_hi - t_lo);
+
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = lane_id();
+  const int n = lane & 15;
+  const int32_t* bt_row = a.kv.bt + (int64_t)b * a.kv.bt_stride;
+  const int T = (k_hi + 63) >> 6;
+  constexpr unsigned kTile = PipeSmem<NRB>::kTile;
+  (void)NW;
+
+  if (w < 4) {
+    // ---- scores and softmax of row blocks 2w, 2w + 1; all tile copies ----
+    // The four softmax waves copy 16 rows each of every K and V tile, so the
+    // PV waves carry no copies, scalar loads or copy waits.
+    TileCopy<4> cp(a.kv, bt_row, g, k_hi);
+    int pg0 = cp.page(0), pg1 = T > 1 ? cp.page(1) : 0, pg2 = T > 2 ? cp.page(2) : 0;
+    const unsigned kbuf = (unsigned)(uintptr_t)(lds_t*)&sm.k[0][0];
+    const unsigned vbuf = (unsigned)(uintptr_t)(lds_t*)&sm.v[0][0];
+    constexpr int kDma = TileCopy<4>::kDma;
+    // Prologue copies: K and V of tiles 0 and 1, K of tile 2.
+    cp.issue(0, pg0, false, kbuf);
+    cp.issue(0, pg0, true, vbuf);
+    if (T > 1) {
+      cp.issue(1, pg1, false, kbuf + kTile);
+      cp.issue(1, pg1, true, vbuf + kTile);
+    }
+    if (T > 2) cp.issue(2, pg2, false, kbuf + 2 * kTile);
+    int pg3 = T > 3 ? cp.page(3) : 0;
+    // Iteration i's wait, barrier and copies (K of tile i + 3, V of tile i + 2).
+    auto open_step = [&](int i) {
+      if (i + 2 < T)
+        wait_vmcnt<2 * kDma>();
+      else if (i + 1 < T)
+        wait_vmcnt<kDma>();
+      else
+        wait_vmcnt<0>();
+      barrier_publish();  // tile i's probabilities are visible; iteration i - 1's reads are done
+      if (i + 3 < T) cp.issue(i + 3, pg3, false, kbuf + ((i + 3) % kPipeStages) * kTile);
+      if (i + 2 < T) cp.issue(i + 2, pg2, true, vbuf + ((i + 2) % kPipeStages) * kTile);
+      pg2 = pg3;
+      pg3 = i + 4 < T ? cp.page(i + 4) : 0;
+    };
+    QFragT<kFP8> qf[2];
+    int klim[2];
+    float c2 = a.c2_base * load_scale(a.q_ds) * load_scale(a.kv.k_ds);
+    const bool flip = c2 < 0.f;  // keep c2 positive: negate the queries instead (sign bit of every FP8 code)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int rr = 16 * (2 * w + j) + n;
+      const bool ok = rr < rows;
+      const int t2 = ok ? rr / a.r : 0;
+      load_q<kFP8, kFP8>(qf[j], a.q, tok0 + t_lo + t2, a.hq, g * a.r + (ok ? rr - t2 * a.r : 0), ok);
+      klim[j] = ok ? min(lk - lq + t_lo + t2, k_hi - 1) : -1;
+      if (flip) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int i = 0; i < 8; ++i) qf[j].hi[h][i] ^= (int)0x80808080u;
+      }
+    }
+    c2 = fmaxf(fabsf(c2), 1e-30f);  // a zero scale: every score counts the same
+    const int min_lim = min(lk - lq + t_lo, k_hi - 1);  // tiles ending at or below it need no mask
+    RowStat rs[2];
+    f32x4 lsum[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      rs[j].init();
+      lsum[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    auto tile = [&](int j, auto masked) {
+      f32x4 s[2][4];
+      tile_scores_rows<2, 4>((const lds_t*)&sm.k[0][0] + (j % kPipeStages) * kTile, qf, s);
+      Exchange<kFP8, NRB>& x = sm.x[j & 1];
+#pragma unroll
+      for (int r = 0; r < 2; ++r)
+        softmax_ws<decltype(masked)::value>(rs[r], lsum[r], s[r], c2, klim[r] - 64 * j, x, 2 * w + r);
+    };
+    wait_vmcnt<0>();
+    barrier();
+    if (63 > min_lim)
+      tile(0, std::true_type{});
+    else
+      tile(0, std::false_type{});
+    // Tiles needing the mask form a suffix, so two loops with one body each.
+    int i = 0;
+    for (; i + 1 < T && 64 * (i + 1) + 63 <= min_lim; ++i) {
+      open_step(i);
+      tile(i + 1, std::false_type{});
+    }
+    for (; i + 1 < T; ++i) {
+      open_step(i);
+      tile(i + 1, std::true_type{});
+    }
+    open_step(T - 1);
+    // Row sums for the PV waves, through the buffer nobody reads in the last
+    // iteration, and the rows' log-sum-exp.
+    Exchange<kFP8, NRB>& xe = sm.x[T & 1];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      if (lane < 16) xe.row[16 * (2 * w + j) + lane] = lsum[j][0];
+      const int rr = 16 * (2 * w + j) + n;
+      if (rr < rows && (lane >> 4) == 0 && a.lse) {
+        const int t2 = rr / a.r;
+        const float lrow = lsum[j][0];
+        a.lse[(tok0 + t_lo + t2) * (int64_t)a.hq + g * a.r + rr - t2 * a.r] =
+            lrow > 0.f ? (rs[j].m + log2f(lrow)) * kLn2 : kNegInf;
+      }
+    }
+    barrier_publish();
+  } else {
+    // ---- PV of head dims 64 (w - 4) .. of all rows ----
+    const int d = w - 4;
+    f32x4 o[4 * NRB];
+#pragma unroll
+    for (int k = 0; k < 4 * NRB; ++k) o[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+    barrier();
+    for (int i = 0; i < T; ++i) {
+      barrier_publish();  // V of tile i has landed (the copying waves waited for it); P(i) is visible
+      pv_ws<NRB>(o, (const lds_t*)&sm.v[0][0] + (i % kPipeStages) * kTile, sm.x[i & 1], d);
+    }
+    barrier_publish();
+    const Exchange<kFP8, NRB>& xe = sm.x[T & 1];
+    const float vds = load_scale(a.kv.v_ds);
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) {
+      const int rr = 16 * rb + n;
+      if (rr < rows) {
+        const int t2 = rr / a.r;
+        const float l = xe.row[rr];
+        const float scale = l > 0.f ? vds / l : 0.f;
+        uint16_t* row_base = a.out + ((tok0 + t_lo + t2) * (int64_t)a.hq + g * a.r + rr - t2 * a.r) * kHeadDim;
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+          const f32x4 v = o[4 * rb + db];
+          *reinterpret_cast<uint2*>(row_base + 64 * d + 16 * db + 4 * (lane >> 4)) =
+              make_uint2(pack_bf16x2(v[0] * scale, v[1] * scale), pack_bf16x2(v[2] * scale, v[3] * scale));
+        }
+      }
+    }
+  }
+}
+
 // The FP8 prefill configuration: waves per workgroup and row blocks per wave.
 // Eight waves of one row block each (two waves per SIMD, 128 rows) measured
 // faster than four waves of two row blocks (one wave per SIMD, whose own
 // latencies then go unhidden).
 constexpr int kPipeWaves = 8;
 constexpr int kPipeRB = 1;
+constexpr bool kWarpSpecialised = true;
 
 int prefill_tile_tokens(int q_dtype, int kv_dtype, int r) {
   if (r <= 0) return 0;
@@ -437,7 +687,12 @@ int prefill_tile_tokens(int q_dtype, int kv_dtype, int r) {
 hipError_t launch_prefill(const PrefillArgs& a, int q_dtype, int kv_dtype, int q_tiles, hipStream_t s) {
   dim3 grid(q_tiles, a.kv.num_kv_heads, a.num_seqs);
   if (q_dtype == kFP8 && kv_dtype == kFP8)
-    hipLaunchKernelGGL((prefill_pipe_kernel<kPipeWaves, kPipeRB>), grid, dim3(64 * kPipeWaves), 0, s, a);
+  {
+    if constexpr (kWarpSpecialised)
+      hipLaunchKernelGGL(prefill_ws_kernel, grid, dim3(512), 0, s, a);
+    else
+      hipLaunchKernelGGL((prefill_pipe_kernel<kPipeWaves, kPipeRB>), grid, dim3(64 * kPipeWaves), 0, s, a);
+  }
   else if (q_dtype == kBF16 && kv_dtype == kFP8)
     hipLaunchKernelGGL((prefill_kernel<kBF16, kFP8, 4>), grid, dim3(256), 0, s, a);
   else
