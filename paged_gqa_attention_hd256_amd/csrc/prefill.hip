@@ -8,8 +8,8 @@
 // kernel, with no gather to contiguous memory first (ROCm/ATOM PR #2830, recipe
 // commit).  Workgroups are ordered longest first.
 //
-// FP8 queries with FP8 keys (the pages' FP8 FMHA) run the software-pipelined
-// prefill_pipe_kernel below; bf16 queries run prefill_kernel, the tile step
+// FP8 queries with FP8 keys (the pages' FP8 FMHA) run the warp-specialised
+// prefill_ws_kernel below; bf16 queries run prefill_kernel, the tile step
 // shared with verify.
 #include <type_traits>
 
@@ -73,33 +73,27 @@ __global__ __launch_bounds__(64 * NW, KV == kFP8 ? 2 : 1) void prefill_kernel(Pr
 }
 
 // ---------------------------------------------------------------------------
-// FP8 queries and keys: a software-pipelined tile loop.
+// FP8 queries and keys: a warp-specialised, software-pipelined tile loop.
 //
-// The tile step above runs a tile's QK^T, softmax and PV back to back, so a
-// wave's vector work (scaling, maxima, exponentials, conversions) and its
-// matrix work follow each other instead of overlapping.  Here iteration i
-// computes the scores of tile i + 1 and, in one straight-line block, the PV
-// product of tile i (matrix cores) together with the softmax of tile i + 1
-// (vector units), so the two kinds of work are in flight at once.  The
-// probabilities are double buffered (tile i's are read while tile i + 1's are
-// written), K and V tiles are triple buffered (copies run two iterations
-// ahead), and one barrier per iteration is enough: it publishes tile i's
-// probabilities and retires every read of the buffers the next copies fill.
-//
-// NW waves hold RB 16-row blocks each (16 NW RB rows); wave w owns the softmax
-// of row blocks RB w .. RB w + RB - 1 and the PV product of head dimensions
-// (256 / NW) w .. of all rows.  With RB = 2 every K fragment read from LDS
-// feeds two row blocks, halving the LDS traffic per row (at the price of one
-// wave per SIMD).
+// The tile step above runs a tile's QK^T, softmax and PV back to back in every
+// wave, so a wave's vector work (scaling, maxima, exponentials, conversions)
+// and its matrix work follow each other.  Here the eight waves of a workgroup
+// (128 rows, one workgroup per CU) split by kind of work:
+//  - waves 0 .. 3 compute scores and softmax, wave w for rows 32 w .. 32 w + 31
+//    (two 16-row blocks sharing every K fragment read from LDS), and issue
+//    every tile copy (16 rows of each K and V tile per wave);
+//  - waves 4 .. 7 compute the PV product, wave 4 + d for head dims
+//    64 d .. 64 d + 63 of all 128 rows.
+// Each SIMD holds one wave of each kind, so the softmax's vector work runs
+// beside the PV matrix work, and every K tile and every tile of probabilities
+// is read from LDS by four waves.  Iteration i: the softmax waves process tile
+// i + 1 while the PV waves multiply tile i.  Probabilities are double buffered
+// (tile i's are read while tile i + 1's are written), K and V tiles triple
+// buffered (copies run two iterations ahead), and one barrier per iteration
+// publishes tile i's probabilities and retires every read of the buffers the
+// next copies fill.
 constexpr int kPipeStages = 3;
-
-template <int NW, int RB>
-struct PipeCfg {
-  static constexpr int kRowBlocks = NW * RB;
-  static constexpr int kRows = 16 * kRowBlocks;
-  static constexpr int kDB = 16 / NW;             // 16-dim blocks of a wave's PV share
-  static constexpr int kAcc = kRowBlocks * kDB;   // f32x4 accumulators per lane
-};
+constexpr int kPipeRows = 128;  // query rows per workgroup
 
 template <int NRB>
 struct PipeSmem {
@@ -173,268 +167,12 @@ struct TileCopy {
   }
 };
 
-// Softmax of one 16-row block (global index rbg) on one tile, straight-line:
+// Softmax of one 16-row block (global block rb) on one tile, straight-line:
 // raw scores s (scaled by c2 > 0 here: max(c2 s) = c2 max(s)), optional mask
-// (key relative to the tile start visible iff <= lim), lazy reference
-// maximum as in softmax_publish, probabilities published as the fp16 B
-// operand, the row rescale factor and the block's rescale flag next to them.
-template <bool MASKED, int NRB>
-__device__ __forceinline__ void softmax_flat(RowStat& rs, f32x4 (&s)[4], float c2, int lim, Exchange<kFP8, NRB>& x,
-                                             int rbg) {
-  const int lane = lane_id();
-  const int gq = lane >> 4, n = lane & 15;
-  float mt = kNegInf;
-#pragma unroll
-  for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if constexpr (MASKED) s[mb][i] = (mb * 16 + 4 * gq + i <= lim) ? s[mb][i] : kNegInf;
-      mt = fmaxf(mt, s[mb][i]);
-    }
-  mt = group4_max(mt);
-  mt = mt == kNegInf ? kNegInf : mt * c2;
-  const bool grow = __builtin_amdgcn_ballot_w64(mt > rs.m + kRescaleLog2) != 0;  // wave-uniform
-  const float m_new = grow ? fmaxf(rs.m, mt) : rs.m;
-  // 1 when the maximum did not move (also before the row's first visible key)
-  const float alpha = m_new == rs.m ? 1.f : fast_exp2(rs.m - m_new);
-  rs.m = m_new;
-  const float nm = m_new == kNegInf ? 0.f : -m_new;
-  // Written by every lane (lanes of one row hold the same values): no branch
-  // splits this straight-line block.
-  x.row[16 * rbg + n] = alpha;
-  x.grow[rbg] = grow;
-#pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    f16x8 pb;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) pb[j] = (_Float16)fast_exp2(__builtin_fmaf(s[2 * t + (j >> 2)][j & 3], c2, nm));
-    x.p[rbg][t][0][lane] = __builtin_bit_cast(i32x4, pb);
-  }
-}
-
-// PV of one tile for this wave's head dimensions of all rows (pv_quarter's
-// arithmetic; the probabilities of one row block are loaded right before
-// their MFMAs, which keeps fewer registers live next to the softmax), and the
-// row sums of the wave's own row blocks from an all-ones A operand.
-template <int NW, int RB, int NA, int NRB>
-__device__ __forceinline__ void pv_pipe(f32x4 (&o)[NA], f32x4 (&lsum)[RB], const lds_t* vt,
-                                        const Exchange<kFP8, NRB>& x, int w) {
-  using G = TileGeom<kFP8>;
-  static_assert(NRB == NW * RB && NA == NRB * (16 / NW), "accumulator layout");
-  constexpr int DB = 16 / NW;
-  const int lane = lane_id();
-  const int gq = lane >> 4, sl = lane & 15;
-  int any = 0;
-#pragma unroll
-  for (int i = 0; i < NRB; ++i) any |= x.grow[i];
-  if (__builtin_amdgcn_readfirstlane(any) != 0) {
-    // The empty asm redefines the accumulators inside this rarely taken
-    // branch, so the compiler cannot compute the rescaled copies on every
-    // tile and select between them (which doubles the live accumulators).
-#pragma unroll
-    for (int i = 0; i < NA; ++i) asm volatile("" : "+v"(o[i]));
-#pragma unroll
-    for (int rb = 0; rb < NRB; ++rb) {
-      const float al = x.row[16 * rb + sl];
-#pragma unroll
-      for (int db = 0; db < DB; ++db) o[DB * rb + db] *= al;
-    }
-#pragma unroll
-    for (int j = 0; j < RB; ++j) lsum[j] *= x.row[16 * (RB * w + j) + sl];
-  }
-  const int e = sl >> 1, q = sl & 1;
-#pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    const int key = 32 * t + 16 * (e >> 2) + 4 * gq + (e & 3);
-    f16x8 a[DB];
-#pragma unroll
-    for (int db = 0; db < DB; ++db) a[db] = fp8x8_to_f16(lds_tr8(vt + G::off(key, DB * w + db) + 8 * q));
-#pragma unroll
-    for (int rb = 0; rb < NRB; ++rb) {
-      const f16x8 pb = __builtin_bit_cast(f16x8, x.p[rb][t][0][lane]);
-#pragma unroll
-      for (int db = 0; db < DB; ++db) o[DB * rb + db] = mfma_f16(a[db], pb, o[DB * rb + db]);
-    }
-    constexpr f16x8 ones = {(_Float16)1.f, (_Float16)1.f, (_Float16)1.f, (_Float16)1.f,
-                            (_Float16)1.f, (_Float16)1.f, (_Float16)1.f, (_Float16)1.f};
-#pragma unroll
-    for (int j = 0; j < RB; ++j)
-      lsum[j] = mfma_f16(ones, __builtin_bit_cast(f16x8, x.p[RB * w + j][t][0][lane]), lsum[j]);
-  }
-}
-
-// Row block rb of a PV share of NA accumulators (16 / NW d-blocks per row
-// block) times `scale`, to a bf16 row of 256 head dimensions.
-template <int NW, int NA>
-__device__ __forceinline__ void store_share_acc(const f32x4 (&o)[NA], int rb, float scale, uint16_t* row_base) {
-  constexpr int DB = 16 / NW;
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int gq = lane_id() >> 4;
-#pragma unroll
-  for (int db = 0; db < DB; ++db) {
-    const f32x4 v = o[DB * rb + db];
-    *reinterpret_cast<uint2*>(row_base + (256 / NW) * w + 16 * db + 4 * gq) =
-        make_uint2(pack_bf16x2(v[0] * scale, v[1] * scale), pack_bf16x2(v[2] * scale, v[3] * scale));
-  }
-}
-
-template <int NW, int RB>
-__global__ __launch_bounds__(64 * NW, 1) void prefill_pipe_kernel(PrefillArgs a) {
-  using C = PipeCfg<NW, RB>;
-  constexpr int NRB = C::kRowBlocks;
-  __shared__ PipeSmem<NRB> sm;
-  const int g = blockIdx.y, b = blockIdx.z;
-  const int tok0 = a.cu_q[b];
-  const int lq = min(a.cu_q[b + 1] - tok0, a.max_q_len);
-  const int lk = min(a.cu_k[b + 1] - a.cu_k[b], a.max_kv_len);
-  const int t_lo = (gridDim.x - 1 - blockIdx.x) * a.tile_tokens;  // longest tiles first
-  if (t_lo >= lq) return;
-  const int t_hi = min(t_lo + a.tile_tokens, lq);
-  const int k_hi = lk - lq + t_hi;
-  const int rows = a.r * (t_hi - t_lo);
-
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int lane = lane_id();
-  const int n = lane & 15;
-  const int32_t* bt_row = a.kv.bt + (int64_t)b * a.kv.bt_stride;
-  const int T = (k_hi + 63) >> 6;
-  TileCopy<NW> cp(a.kv, bt_row, g, k_hi);
-  int pg0 = cp.page(0), pg1 = T > 1 ? cp.page(1) : 0, pg2 = T > 2 ? cp.page(2) : 0;
-
-  // This wave's softmax rows: row blocks RB w + j, lane row 16 (RB w + j) + n.
-  QFragT<kFP8> qf[RB];
-  int klim[RB];
-  float c2 = a.c2_base * load_scale(a.q_ds) * load_scale(a.kv.k_ds);
-  const bool flip = c2 < 0.f;  // keep c2 positive: negate the queries instead (sign bit of every FP8 code)
-#pragma unroll
-  for (int j = 0; j < RB; ++j) {
-    const int rr = 16 * (RB * w + j) + n;
-    const bool ok = rr < rows;
-    const int t2 = ok ? rr / a.r : 0;
-    load_q<kFP8, kFP8>(qf[j], a.q, tok0 + t_lo + t2, a.hq, g * a.r + (ok ? rr - t2 * a.r : 0), ok);
-    klim[j] = ok ? min(lk - lq + t_lo + t2, k_hi - 1) : -1;
-    if (flip) {
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int i = 0; i < 8; ++i) qf[j].hi[h][i] ^= (int)0x80808080u;
-    }
-  }
-  c2 = fmaxf(fabsf(c2), 1e-30f);  // a zero scale: every score counts the same
-  const int min_lim = min(lk - lq + t_lo, k_hi - 1);  // tiles ending at or below it need no mask
-
-  const unsigned kbuf = (unsigned)(uintptr_t)(lds_t*)&sm.k[0][0];
-  const unsigned vbuf = (unsigned)(uintptr_t)(lds_t*)&sm.v[0][0];
-  constexpr unsigned kTile = PipeSmem<NRB>::kTile;
-  constexpr int kDma = TileCopy<NW>::kDma;
-
-  // Prologue: K and V of tiles 0 and 1, K of tile 2; scores and softmax of tile 0.
-  cp.issue(0, pg0, false, kbuf);
-  cp.issue(0, pg0, true, vbuf);
-  if (T > 1) {
-    cp.issue(1, pg1, false, kbuf + kTile);
-    cp.issue(1, pg1, true, vbuf + kTile);
-  }
-  if (T > 2) cp.issue(2, pg2, false, kbuf + 2 * kTile);
-  int pg3 = T > 3 ? cp.page(3) : 0;
-  wait_vmcnt<0>();
-  barrier();
-  RowStat rs[RB];
-  f32x4 o[C::kAcc];
-#pragma unroll
-  for (int i = 0; i < C::kAcc; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  f32x4 lsum[RB];
-#pragma unroll
-  for (int j = 0; j < RB; ++j) {
-    rs[j].init();
-    lsum[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-  auto softmax_all = [&](f32x4 (&s)[RB][4], int tb, auto masked, Exchange<kFP8, NRB>& x) {
-#pragma unroll
-    for (int j = 0; j < RB; ++j)
-      softmax_flat<decltype(masked)::value>(rs[j], s[j], c2, klim[j] - tb, x, RB * w + j);
-  };
-  {
-    f32x4 s[RB][4];
-    tile_scores_rows<RB, 4>((const lds_t*)&sm.k[0][0], qf, s);
-    if (63 > min_lim)
-      softmax_all(s, 0, std::true_type{}, sm.x[0]);
-    else
-      softmax_all(s, 0, std::false_type{}, sm.x[0]);
-  }
-
-  // Iteration i: tile i's PV, tile i + 1's scores and softmax.
-  auto step = [&](int i, auto masked_next, auto has_next) {
-    constexpr bool kNext = decltype(has_next)::value;
-    // K(i + 1) and V(i) have landed when at most the copies of iteration i - 1
-    // (K(i + 2), V(i + 1)) are still in flight.
-    if (i + 2 < T)
-      wait_vmcnt<2 * kDma>();
-    else if (i + 1 < T)
-      wait_vmcnt<kDma>();
-    else
-      wait_vmcnt<0>();
-    barrier_publish();  // tile i's probabilities are visible; iteration i - 1's reads are done
-    if (i + 3 < T) cp.issue(i + 3, pg3, false, kbuf + ((i + 3) % kPipeStages) * kTile);
-    if (i + 2 < T) cp.issue(i + 2, pg2, true, vbuf + ((i + 2) % kPipeStages) * kTile);
-    pg2 = pg3;
-    pg3 = i + 4 < T ? cp.page(i + 4) : 0;
-    f32x4 s[RB][4];
-    if constexpr (kNext)
-      tile_scores_rows<RB, 4>((const lds_t*)&sm.k[0][0] + ((i + 1) % kPipeStages) * kTile, qf, s);
-    pv_pipe<NW, RB>(o, lsum, (const lds_t*)&sm.v[0][0] + (i % kPipeStages) * kTile, sm.x[i & 1], w);
-    if constexpr (kNext) softmax_all(s, 64 * (i + 1), masked_next, sm.x[(i + 1) & 1]);
-  };
-  // Tiles needing the mask form a suffix (they end past min_lim), so three
-  // loops with one body each keep the accumulators in fixed registers.
-  int i = 0;
-  for (; i + 1 < T && 64 * (i + 1) + 63 <= min_lim; ++i) step(i, std::false_type{}, std::true_type{});
-  for (; i + 1 < T; ++i) step(i, std::true_type{}, std::true_type{});
-  step(T - 1, std::false_type{}, std::false_type{});
-
-  // Row sums through the buffer no wave reads in the last iteration.
-  Exchange<kFP8, NRB>& xe = sm.x[T & 1];
-  if (lane < 16) {
-#pragma unroll
-    for (int j = 0; j < RB; ++j) xe.row[16 * (RB * w + j) + lane] = lsum[j][0];
-  }
-  barrier_publish();
-#pragma unroll
-  for (int j = 0; j < RB; ++j) {
-    const int rr = 16 * (RB * w + j) + n;
-    if (rr < rows && (lane >> 4) == 0 && a.lse) {
-      const int t2 = rr / a.r;
-      const float lrow = lsum[j][0];
-      a.lse[(tok0 + t_lo + t2) * (int64_t)a.hq + g * a.r + rr - t2 * a.r] =
-          lrow > 0.f ? (rs[j].m + log2f(lrow)) * kLn2 : kNegInf;
-    }
-  }
-  const float vds = load_scale(a.kv.v_ds);
-#pragma unroll
-  for (int rb = 0; rb < NRB; ++rb) {
-    const int rr = 16 * rb + n;
-    if (rr < rows) {
-      const int t2 = rr / a.r;
-      const float l = xe.row[rr];
-      store_share_acc<NW, C::kAcc>(o, rb, l > 0.f ? vds / l : 0.f,
-                                   a.out + ((tok0 + t_lo + t2) * (int64_t)a.hq + g * a.r + rr - t2 * a.r) * kHeadDim);
-    }
-  }
-}
-
-// Warp-specialised schedule for FP8 Q and KV (128 rows, eight waves, one
-// workgroup per CU).  Waves 0 .. 3 compute scores and softmax, wave w for
-// rows 32 w .. 32 w + 31 (two 16-row blocks sharing every K fragment read
-// from LDS); waves 4 .. 7 compute the PV product, wave 4 + d for head dims
-// 64 d .. 64 d + 63 of all 128 rows.  Each SIMD holds one wave of each kind,
-// so the vector work of the softmax runs beside the matrix work of PV, and
-// each K tile and each tile of probabilities is read from LDS by four waves
-// instead of eight.  Iteration i: the softmax waves process tile i + 1 while
-// the PV waves multiply tile i; probabilities are double buffered, K and V
-// triple buffered as in prefill_pipe_kernel, one barrier per iteration.
-
-// Softmax of one 16-row block (rows of global block rb) on one tile, as
-// softmax_flat, also keeping the block's running row sums (all-ones A operand).
+// (key relative to the tile start visible iff <= lim), lazy reference maximum
+// as in softmax_publish, probabilities published as the fp16 B operand with
+// the row rescale factors and the block's rescale flag next to them, and the
+// block's running row sums from an all-ones A operand.
 template <bool MASKED, int NRB>
 __device__ __forceinline__ void softmax_ws(RowStat& rs, f32x4& lsum, f32x4 (&s)[4], float c2, int lim,
                                            Exchange<kFP8, NRB>& x, int rb) {
@@ -519,7 +257,7 @@ __device__ __forceinline__ void pv_ws(f32x4 (&o)[4 * NRB], const lds_t* vt, cons
 }
 
 __global__ __launch_bounds__(512, 1) void prefill_ws_kernel(PrefillArgs a) {
-  constexpr int NW = 8, NRB = 8;
+  constexpr int NRB = kPipeRows / 16;  // row blocks of the workgroup
   __shared__ PipeSmem<NRB> sm;
   const int g = blockIdx.y, b = blockIdx.z;
   const int tok0 = a.cu_q[b];
@@ -537,7 +275,6 @@ __global__ __launch_bounds__(512, 1) void prefill_ws_kernel(PrefillArgs a) {
   const int32_t* bt_row = a.kv.bt + (int64_t)b * a.kv.bt_stride;
   const int T = (k_hi + 63) >> 6;
   constexpr unsigned kTile = PipeSmem<NRB>::kTile;
-  (void)NW;
 
   if (w < 4) {
     // ---- scores and softmax of row blocks 2w, 2w + 1; all tile copies ----
@@ -671,28 +408,15 @@ __global__ __launch_bounds__(512, 1) void prefill_ws_kernel(PrefillArgs a) {
   }
 }
 
-// The FP8 prefill configuration: waves per workgroup and row blocks per wave.
-// Eight waves of one row block each (two waves per SIMD, 128 rows) measured
-// faster than four waves of two row blocks (one wave per SIMD, whose own
-// latencies then go unhidden).
-constexpr int kPipeWaves = 8;
-constexpr int kPipeRB = 1;
-constexpr bool kWarpSpecialised = true;
-
 int prefill_tile_tokens(int q_dtype, int kv_dtype, int r) {
   if (r <= 0) return 0;
-  return (q_dtype == kFP8 && kv_dtype == kFP8) ? PipeCfg<kPipeWaves, kPipeRB>::kRows / r : 64 / r;
+  return (q_dtype == kFP8 && kv_dtype == kFP8) ? kPipeRows / r : 64 / r;
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, int q_dtype, int kv_dtype, int q_tiles, hipStream_t s) {
   dim3 grid(q_tiles, a.kv.num_kv_heads, a.num_seqs);
   if (q_dtype == kFP8 && kv_dtype == kFP8)
-  {
-    if constexpr (kWarpSpecialised)
-      hipLaunchKernelGGL(prefill_ws_kernel, grid, dim3(512), 0, s, a);
-    else
-      hipLaunchKernelGGL((prefill_pipe_kernel<kPipeWaves, kPipeRB>), grid, dim3(64 * kPipeWaves), 0, s, a);
-  }
+    hipLaunchKernelGGL(prefill_ws_kernel, grid, dim3(512), 0, s, a);
   else if (q_dtype == kBF16 && kv_dtype == kFP8)
     hipLaunchKernelGGL((prefill_kernel<kBF16, kFP8, 4>), grid, dim3(256), 0, s, a);
   else
