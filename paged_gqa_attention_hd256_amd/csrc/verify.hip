@@ -19,6 +19,8 @@
 // exp(lse - max lse).  This replaces a fixed segment count, which on a batch
 // of uneven lengths leaves a nearly empty second round of workgroups
 // (Modifications: segments chosen from CU parallelism and per-segment work).
+#include <type_traits>
+
 #include "causal_stream.h"
 
 namespace pga {
@@ -281,12 +283,39 @@ __global__ __launch_bounds__(256) void verify_merge_kernel(VerifyArgs a) {
     const int excl = incl - cnt;
     const int nseg = min(64, sw.segs - s0);
     const int np = __shfl(incl, nseg - 1);  // pieces of these segments
+    // This lane's 4 head dimensions of the row in piece slot sl, as stored
+    // (fp16 for FP8 V, fp32 for BF16 V), and widened to fp32.
+    using Raw = std::conditional_t<KV == kFP8, uint2, f32x4>;
+    auto load_part = [&](int sl) -> Raw {
+      const int64_t off = ((int64_t)sl * a.rows_cap + rho) * kHeadDim + 4 * lane;
+      if constexpr (KV == kFP8)
+        return *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(a.ws_o) + off);
+      else
+        return *reinterpret_cast<const f32x4*>(static_cast<const float*>(a.ws_o) + off);
+    };
+    auto widen = [](Raw r) -> f32x4 {
+      if constexpr (KV == kFP8) {
+        const f16x4 h = __builtin_bit_cast(f16x4, r);
+        return f32x4{(float)h[0], (float)h[1], (float)h[2], (float)h[3]};
+      } else {
+        return r;
+      }
+    };
     for (int c = 0; c < np; c += 64) {
       const int j = c + lane;
       int sj = 0;
       for (int k = 1; k < nseg; ++k) sj = j >= __builtin_amdgcn_readlane(excl, k) ? k : sj;
       const int slot = j < np ? su + s0 + sj + __shfl(first, sj) + (j - __shfl(excl, sj)) : -1;
       const float ls = slot >= 0 ? a.ws_lse[(int64_t)slot * a.rows_cap + rho] : kNegInf;
+      // The rows of up to 16 pieces are requested with their lse values (one
+      // round trip for the usual piece counts); no load past the last piece.
+      const int n = min(64, np - c);
+      Raw v[16];
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        v[k] = Raw{};
+        if (k < n) v[k] = load_part(__builtin_amdgcn_readlane(slot, k));  // wave-uniform
+      }
       // Online merge of this batch of pieces into (mx, wsum, acc).
       const float mb = wave_max(ls);
       if (mb == kNegInf) continue;
@@ -297,33 +326,19 @@ __global__ __launch_bounds__(256) void verify_merge_kernel(VerifyArgs a) {
       mx = m_new;
       const float wgt = ls == kNegInf ? 0.f : __expf(ls - mx);
       wsum += wave_sum(wgt);
-      // This lane's 4 head dimensions of the row in piece slot sl.
-      auto part = [&](int sl) -> f32x4 {
-        const int64_t off = ((int64_t)sl * a.rows_cap + rho) * kHeadDim + 4 * lane;
-        if constexpr (KV == kFP8) {
-          const f16x4 h = *reinterpret_cast<const f16x4*>(static_cast<const uint16_t*>(a.ws_o) + off);
-          return f32x4{(float)h[0], (float)h[1], (float)h[2], (float)h[3]};
-        } else {
-          return *reinterpret_cast<const f32x4*>(static_cast<const float*>(a.ws_o) + off);
-        }
-      };
-      // Rows of 8 pieces in flight at a time; past the last piece the weight
-      // is 0 and the slot repeats the last one, so the loads stay in bounds.
-      const int n = min(64, np - c);
-      const int last = __builtin_amdgcn_readlane(slot, n - 1);
-      for (int q = 0; q < n; q += 8) {
-        f32x4 v[8];
-        float wq[8];
+      for (int q = 0; q < n; q += 16) {
+        if (q > 0) {
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          const int src = min(q + k, 63);
-          const int sl = __builtin_amdgcn_readlane(slot, src);
-          wq[k] = q + k < n ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wgt), src)) : 0.f;
-          v[k] = part(q + k < n ? sl : last);
+          for (int k = 0; k < 16; ++k) {
+            v[k] = Raw{};
+            if (q + k < n) v[k] = load_part(__builtin_amdgcn_readlane(slot, q + k));  // wave-uniform
+          }
         }
 #pragma unroll
-        for (int k = 0; k < 8; ++k)
-          if (wq[k] != 0.f) acc += wq[k] * v[k];
+        for (int k = 0; k < 16; ++k) {
+          const float wq = q + k < n ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wgt), q + k)) : 0.f;
+          if (wq != 0.f) acc += wq * widen(v[k]);
+        }
       }
     }
   }
