@@ -45,7 +45,13 @@ __device__ __forceinline__ int seq_of(const int32_t* cu_q, int num_seqs, int tok
   return lo;
 }
 
-template <int KV>
+// DENSE: the pool's token rows are evenly spaced (page stride = page_size x
+// token stride, for K and for V; the "NHD" layout), the token strides fit 32
+// bits and every physical row index fits 31 bits.  Then a row's address is one
+// 32 x 32 -> 64-bit multiply-add of its physical row index onto a per-lane
+// base, instead of splitting the index into page and slot and forming two
+// 64-bit products (address arithmetic is most of this kernel's vector work).
+template <int KV, bool DENSE>
 __global__ __launch_bounds__(SparseCfg<KV>::kWaves * 64) void sparse_kernel(SparseArgs a) {
   using C = SparseCfg<KV>;
   using G = typename C::G;
@@ -85,6 +91,18 @@ __global__ __launch_bounds__(SparseCfg<KV>::kWaves * 64) void sparse_kernel(Spar
 
   WaveState st;
   st.init();
+  // Per-lane parts of the DMA source addresses that do not change from tile
+  // to tile: the 16-byte chunk this lane copies of its row (swizzled by row).
+  const uint64_t zaddr = (uint64_t)(uintptr_t)g_zero16;
+  const uint32_t kst = (uint32_t)a.kv.k_st, vst = (uint32_t)a.kv.v_st;
+  uint64_t kb[C::kDmaPerTile], vb[C::kDmaPerTile];
+#pragma unroll
+  for (int u = 0; u < C::kDmaPerTile; ++u) {
+    const int row = u * C::kRowsPerDma + lane / G::kChunks;
+    const int chunk = (lane % G::kChunks) ^ (row & (G::kChunks - 1));
+    kb[u] = (uint64_t)(uintptr_t)kbase + chunk * 16;
+    vb[u] = (uint64_t)(uintptr_t)vbase + chunk * 16;
+  }
 
   const int e_end = min((sp + 1) * a.split_len, a.num_selected);
   for (int c0 = sp * a.split_len; c0 < e_end; c0 += kSparseTableEntries) {
@@ -107,17 +125,21 @@ __global__ __launch_bounds__(SparseCfg<KV>::kWaves * 64) void sparse_kernel(Spar
 #pragma unroll
       for (int u = 0; u < C::kDmaPerTile; ++u) {
         const int row0 = u * C::kRowsPerDma;
-        const int row = row0 + lane / G::kChunks;
-        const int chunk = (lane % G::kChunks) ^ (row & (G::kChunks - 1));
-        const int phys = lds_load<int>(table + 4 * (it * C::kTileKeys + row));
-        const int64_t page = phys >> a.kv.page_shift;
-        const int slot = phys & pmask;
-        const uint8_t* ks = phys >= 0 ? kbase + page * a.kv.k_sp + slot * a.kv.k_st + chunk * 16
-                                      : reinterpret_cast<const uint8_t*>(g_zero16);
-        const uint8_t* vs = phys >= 0 ? vbase + page * a.kv.v_sp + slot * a.kv.v_st + chunk * 16
-                                      : reinterpret_cast<const uint8_t*>(g_zero16);
-        dma16(ks, tiles + (2 * buf + 0) * C::kTileBytes + row0 * G::kRowBytes);
-        dma16(vs, tiles + (2 * buf + 1) * C::kTileBytes + row0 * G::kRowBytes);
+        const int phys = lds_load<int>(table + 4 * (it * C::kTileKeys + row0 + lane / G::kChunks));
+        uint64_t ks, vs;
+        if constexpr (DENSE) {
+          ks = phys >= 0 ? (uint64_t)(uint32_t)phys * kst + kb[u] : zaddr;
+          vs = phys >= 0 ? (uint64_t)(uint32_t)phys * vst + vb[u] : zaddr;
+        } else {
+          const int row = row0 + lane / G::kChunks;
+          const int chunk = (lane % G::kChunks) ^ (row & (G::kChunks - 1));
+          const int64_t page = phys >> a.kv.page_shift;
+          const int slot = phys & pmask;
+          ks = phys >= 0 ? (uint64_t)(uintptr_t)(kbase + page * a.kv.k_sp + slot * a.kv.k_st + chunk * 16) : zaddr;
+          vs = phys >= 0 ? (uint64_t)(uintptr_t)(vbase + page * a.kv.v_sp + slot * a.kv.v_st + chunk * 16) : zaddr;
+        }
+        dma16((const void*)(uintptr_t)ks, tiles + (2 * buf + 0) * C::kTileBytes + row0 * G::kRowBytes);
+        dma16((const void*)(uintptr_t)vs, tiles + (2 * buf + 1) * C::kTileBytes + row0 * G::kRowBytes);
       }
     };
 
@@ -228,10 +250,21 @@ hipError_t launch_sparse(const SparseArgs& a, int kv_dtype, hipStream_t s) {
   constexpr int W = 4;  // waves per workgroup, both encodings
   static_assert(SparseCfg<kFP8>::kWaves == W && SparseCfg<kBF16>::kWaves == W, "launch shape");
   const dim3 grid((unsigned)((jobs + W - 1) / W));
-  if (kv_dtype == kFP8)
-    hipLaunchKernelGGL(sparse_kernel<kFP8>, grid, dim3(W * 64), 0, s, a);
-  else
-    hipLaunchKernelGGL(sparse_kernel<kBF16>, grid, dim3(W * 64), 0, s, a);
+  const KvArgs& kv = a.kv;
+  const bool dense = kv.k_sp == (int64_t)kv.page_size * kv.k_st && kv.v_sp == (int64_t)kv.page_size * kv.v_st &&
+                     kv.k_st > 0 && kv.v_st > 0 && kv.k_st < (int64_t(1) << 32) && kv.v_st < (int64_t(1) << 32) &&
+                     (int64_t)kv.num_pages * kv.page_size < (int64_t(1) << 31);
+  if (kv_dtype == kFP8) {
+    if (dense)
+      hipLaunchKernelGGL((sparse_kernel<kFP8, true>), grid, dim3(W * 64), 0, s, a);
+    else
+      hipLaunchKernelGGL((sparse_kernel<kFP8, false>), grid, dim3(W * 64), 0, s, a);
+  } else {
+    if (dense)
+      hipLaunchKernelGGL((sparse_kernel<kBF16, true>), grid, dim3(W * 64), 0, s, a);
+    else
+      hipLaunchKernelGGL((sparse_kernel<kBF16, false>), grid, dim3(W * 64), 0, s, a);
+  }
   if (a.splits > 1) {
     if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
     const dim3 mgrid((unsigned)(((int64_t)a.num_tokens * a.hq + 3) / 4));
