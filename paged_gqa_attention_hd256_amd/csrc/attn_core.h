@@ -132,6 +132,20 @@ __device__ __forceinline__ void tile_scores(const lds_t* kt, const QFragT<KV>& q
         for (int mb = 0; mb < NMB; ++mb) s[mb] = mfma_fp8_scaled(a[mb], qf.lo[h], s[mb], kScaleLo);
       }
     }
+  } else if constexpr (NMB == 1) {
+    // One 16-key block: every K fragment is requested first, and the head
+    // dimension is summed in two chains (even and odd 32-element steps) so
+    // that consecutive MFMAs do not wait on each other's results.
+    bf16x8 a[8];
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) a[ks] = lds_load<bf16x8>(kt + G::off(n, 4 * ks + gq));
+    f32x4 s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 8; ks += 2) {
+      s[0] = mfma_bf16(a[ks], qf.q[ks], s[0]);
+      s1 = mfma_bf16(a[ks + 1], qf.q[ks + 1], s1);
+    }
+    s[0] += s1;
   } else {
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
@@ -216,12 +230,17 @@ __device__ __forceinline__ void tile_pv(WaveState& st, const lds_t* vt, const f3
       ph[j] = __builtin_bit_cast(short, h);
       pl[j] = __builtin_bit_cast(short, (__bf16)(x - (float)h));
     }
+    // Every V fragment first, then the high parts of all 16 blocks and the
+    // low parts (the same sums per block as high-then-low, without a product
+    // waiting on the one just before it).
+    i16x4 a[16];
 #pragma unroll
-    for (int mb = 0; mb < 16; ++mb) {
-      const i16x4 a = __builtin_bit_cast(i16x4, lds_tr16(vt + G::off(4 * gq + e, 2 * mb + (q >> 1)) + 8 * (q & 1)));
-      st.o[mb] = mfma_bf16_k16(a, ph, st.o[mb]);
-      st.o[mb] = mfma_bf16_k16(a, pl, st.o[mb]);
-    }
+    for (int mb = 0; mb < 16; ++mb)
+      a[mb] = __builtin_bit_cast(i16x4, lds_tr16(vt + G::off(4 * gq + e, 2 * mb + (q >> 1)) + 8 * (q & 1)));
+#pragma unroll
+    for (int mb = 0; mb < 16; ++mb) st.o[mb] = mfma_bf16_k16(a[mb], ph, st.o[mb]);
+#pragma unroll
+    for (int mb = 0; mb < 16; ++mb) st.o[mb] = mfma_bf16_k16(a[mb], pl, st.o[mb]);
     return;
   }
   static_assert(NMB % 2 == 0 || (KV == kBF16 && NMB == 1), "tiles hold a multiple of 32 keys");

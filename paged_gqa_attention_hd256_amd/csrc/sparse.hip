@@ -51,8 +51,11 @@ __device__ __forceinline__ int seq_of(const int32_t* cu_q, int num_seqs, int tok
 // 32 x 32 -> 64-bit multiply-add of its physical row index onto a per-lane
 // base, instead of splitting the index into page and slot and forming two
 // 64-bit products (address arithmetic is most of this kernel's vector work).
+// One wave per SIMD (the LDS holds four waves' buffers per CU), so the
+// compiler may spend registers on keeping more loads in flight.
 template <int KV, bool DENSE>
-__global__ __launch_bounds__(SparseCfg<KV>::kWaves * 64) void sparse_kernel(SparseArgs a) {
+__global__ __launch_bounds__(SparseCfg<KV>::kWaves * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void sparse_kernel(SparseArgs a) {
   using C = SparseCfg<KV>;
   using G = typename C::G;
   __shared__ __attribute__((aligned(16))) char smem[C::kWaves][C::kWaveBytes];
@@ -122,10 +125,16 @@ __global__ __launch_bounds__(SparseCfg<KV>::kWaves * 64) void sparse_kernel(Spar
     }
 
     auto issue = [&](int it, int buf) {
+      // Every table read of the tile first, so their LDS latency is paid once
+      // (the copies below are ordered memory operations: no load moves past them).
+      int physv[C::kDmaPerTile];
+#pragma unroll
+      for (int u = 0; u < C::kDmaPerTile; ++u)
+        physv[u] = lds_load<int>(table + 4 * (it * C::kTileKeys + u * C::kRowsPerDma + lane / G::kChunks));
 #pragma unroll
       for (int u = 0; u < C::kDmaPerTile; ++u) {
         const int row0 = u * C::kRowsPerDma;
-        const int phys = lds_load<int>(table + 4 * (it * C::kTileKeys + row0 + lane / G::kChunks));
+        const int phys = physv[u];
         uint64_t ks, vs;
         if constexpr (DENSE) {
           ks = phys >= 0 ? (uint64_t)(uint32_t)phys * kst + kb[u] : zaddr;
