@@ -139,6 +139,7 @@ __device__ __forceinline__ void tile_scores(const lds_t* kt, const QFragT<KV>& q
     bf16x8 a[8];
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) a[ks] = lds_load<bf16x8>(kt + G::off(n, 4 * ks + gq));
+    __builtin_amdgcn_sched_barrier(0);  // keep the requests ahead of the products
     f32x4 s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < 8; ks += 2) {
@@ -237,6 +238,7 @@ __device__ __forceinline__ void tile_pv(WaveState& st, const lds_t* vt, const f3
 #pragma unroll
     for (int mb = 0; mb < 16; ++mb)
       a[mb] = __builtin_bit_cast(i16x4, lds_tr16(vt + G::off(4 * gq + e, 2 * mb + (q >> 1)) + 8 * (q & 1)));
+    __builtin_amdgcn_sched_barrier(0);  // keep the requests ahead of the products
 #pragma unroll
     for (int mb = 0; mb < 16; ++mb) st.o[mb] = mfma_bf16_k16(a[mb], ph, st.o[mb]);
 #pragma unroll
@@ -256,11 +258,13 @@ __device__ __forceinline__ void tile_pv(WaveState& st, const lds_t* vt, const f3
       // transpose-read source: lane sl = 2e + q points at key(e), bytes 8q..8q+7 of the d-block
       const int e = sl >> 1, q = sl & 1;
       const int key = 32 * t + 16 * (e >> 2) + 4 * gq + (e & 3);
+      // Every V fragment of the 32-key step is requested before the first product.
+      i32x2 raw[16];
 #pragma unroll
-      for (int mb = 0; mb < 16; ++mb) {
-        const f16x8 a = fp8x8_to_f16(lds_tr8(vt + G::off(key, mb) + 8 * q));
-        st.o[mb] = mfma_f16(a, pb, st.o[mb]);
-      }
+      for (int mb = 0; mb < 16; ++mb) raw[mb] = lds_tr8(vt + G::off(key, mb) + 8 * q);
+      __builtin_amdgcn_sched_barrier(0);  // keep the requests ahead of the products
+#pragma unroll
+      for (int mb = 0; mb < 16; ++mb) st.o[mb] = mfma_f16(fp8x8_to_f16(raw[mb]), pb, st.o[mb]);
     } else {
       bf16x8 ph, pl;
 #pragma unroll
