@@ -45,6 +45,48 @@ __device__ __forceinline__ int seq_of(const int32_t* cu_q, int num_seqs, int tok
   return lo;
 }
 
+// Online-softmax step of one tile that leaves the accumulators alone: the
+// scores become probabilities in place and the row maximum and sum move on;
+// the returned factor is what the accumulators must be multiplied by before
+// this tile's product is added (1 unless the reference maximum moved; `grow`
+// is set, wave-uniformly, when some row's did).  No branch, so it can run
+// between the products of the previous tile.  The reference maximum moves
+// only when a tile's maximum exceeds it by more than kRescaleLog2, as in
+// tile_softmax.
+template <int NMB, class Vis>
+__device__ __forceinline__ float softmax_deferred(float& m, float& l, f32x4 (&s)[NMB], float c2, Vis visible,
+                                                  bool& grow) {
+  const int gq = lane_id() >> 4;
+  float mt = kNegInf;
+#pragma unroll
+  for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float x = visible(mb * 16 + 4 * gq + i) ? s[mb][i] * c2 : kNegInf;
+      s[mb][i] = x;
+      mt = fmaxf(mt, x);
+    }
+  mt = group4_max(mt);
+  grow = __builtin_amdgcn_ballot_w64(mt > m + kRescaleLog2) != 0;
+  const float m_new = grow ? fmaxf(m, mt) : m;
+  // 0 when m is -inf and the row now has a key; 1 when its maximum did not move.
+  const float alpha = m_new == m ? 1.f : fast_exp2(m - m_new);
+  l *= alpha;
+  m = m_new;
+  const float m_use = m == kNegInf ? 0.f : m;
+  float sum = 0.f;
+#pragma unroll
+  for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float pv = fast_exp2(s[mb][i] - m_use);
+      s[mb][i] = pv;
+      sum += pv;
+    }
+  l += sum;
+  return alpha;
+}
+
 // DENSE: the pool's token rows are evenly spaced (page stride = page_size x
 // token stride, for K and for V; the "NHD" layout), the token strides fit 32
 // bits and every physical row index fits 31 bits.  Then a row's address is one
@@ -124,7 +166,8 @@ void sparse_kernel(SparseArgs a) {
       lds_store<int>(table + 4 * e, phys);
     }
 
-    auto issue = [&](int it, int buf) {
+    // Copies of one operand (K or V) of tile it into stage buf.
+    auto issue = [&](int it, int buf, bool is_v) {
       // Every table read of the tile first, so their LDS latency is paid once
       // (the copies below are ordered memory operations: no load moves past them).
       int physv[C::kDmaPerTile];
@@ -135,47 +178,76 @@ void sparse_kernel(SparseArgs a) {
       for (int u = 0; u < C::kDmaPerTile; ++u) {
         const int row0 = u * C::kRowsPerDma;
         const int phys = physv[u];
-        uint64_t ks, vs;
+        uint64_t src;
         if constexpr (DENSE) {
-          ks = phys >= 0 ? (uint64_t)(uint32_t)phys * kst + kb[u] : zaddr;
-          vs = phys >= 0 ? (uint64_t)(uint32_t)phys * vst + vb[u] : zaddr;
+          src = phys >= 0 ? (uint64_t)(uint32_t)phys * (is_v ? vst : kst) + (is_v ? vb[u] : kb[u]) : zaddr;
         } else {
           const int row = row0 + lane / G::kChunks;
           const int chunk = (lane % G::kChunks) ^ (row & (G::kChunks - 1));
           const int64_t page = phys >> a.kv.page_shift;
           const int slot = phys & pmask;
-          ks = phys >= 0 ? (uint64_t)(uintptr_t)(kbase + page * a.kv.k_sp + slot * a.kv.k_st + chunk * 16) : zaddr;
-          vs = phys >= 0 ? (uint64_t)(uintptr_t)(vbase + page * a.kv.v_sp + slot * a.kv.v_st + chunk * 16) : zaddr;
+          src = phys >= 0 ? (uint64_t)(uintptr_t)((is_v ? vbase : kbase) + page * (is_v ? a.kv.v_sp : a.kv.k_sp) +
+                                                  slot * (is_v ? a.kv.v_st : a.kv.k_st) + chunk * 16)
+                          : zaddr;
         }
-        dma16((const void*)(uintptr_t)ks, tiles + (2 * buf + 0) * C::kTileBytes + row0 * G::kRowBytes);
-        dma16((const void*)(uintptr_t)vs, tiles + (2 * buf + 1) * C::kTileBytes + row0 * G::kRowBytes);
+        dma16((const void*)(uintptr_t)src, tiles + (2 * buf + (is_v ? 1 : 0)) * C::kTileBytes + row0 * G::kRowBytes);
       }
     };
-
-    issue(0, 0);
-    for (int it = 0; it < ntiles; ++it) {
-      if (it + 1 < ntiles) {
-        issue(it + 1, (it + 1) & 1);
-        wait_vmcnt<2 * C::kDmaPerTile>();
-      } else {
-        wait_vmcnt<0>();
-      }
-      const lds_t* kt = tiles + (2 * (it & 1) + 0) * C::kTileBytes;
-      const lds_t* vt = tiles + (2 * (it & 1) + 1) * C::kTileBytes;
-      f32x4 sc[C::kBlocks];
-      tile_scores<KV, C::kBlocks, true>(kt, qf, sc);
+    // Scores and softmax of tile it (K in stage it & 1); the accumulators are
+    // left for the caller to rescale after the previous tile's product.
+    auto scores_softmax = [&](int it, f32x4 (&sc)[C::kBlocks], bool& grow) -> float {
+      tile_scores<KV, C::kBlocks, true>(tiles + (2 * (it & 1) + 0) * C::kTileBytes, qf, sc);
       const lds_t* tt = table + 4 * (it * C::kTileKeys);
       const i32x4 v0 = lds_load<i32x4>(tt + 4 * (4 * gq));
       i32x4 v1 = v0;
       if constexpr (C::kBlocks == 2) v1 = lds_load<i32x4>(tt + 4 * (16 + 4 * gq));
-      tile_softmax<true>(st, sc, c2, [&](int key) {
+      return softmax_deferred(st.m, st.l, sc, c2, [&](int key) {
         const int q = key - 4 * gq;  // 0..3 in block 0, 16..19 in block 1
         const int e = q & 3;
         const int v = (q < 16) ? v0[e] : v1[e];
         return v >= 0;
-      });
-      tile_pv<KV, C::kBlocks>(st, vt, sc);
+      }, grow);
+    };
+
+    // Software pipeline: iteration it computes the scores and softmax of tile
+    // it + 1 and the product of tile it, so neither waits on the other's
+    // latencies.  K runs two tiles ahead of the product, V one: K(it + 2) goes
+    // into the K stage of tile it (its scores were computed an iteration
+    // earlier), V(it + 1) into the V stage of tile it - 1.
+    constexpr int D = C::kDmaPerTile;
+    issue(0, 0, false);
+    issue(0, 0, true);
+    if (ntiles > 1) {
+      issue(1, 1, false);
+      wait_vmcnt<2 * D>();  // K(0)
+    } else {
+      wait_vmcnt<D>();
     }
+    f32x4 p[C::kBlocks];
+    bool grow;
+    scores_softmax(0, p, grow);  // the accumulators are still zero
+    for (int it = 0; it + 1 < ntiles; ++it) {
+      if (it + 2 < ntiles) {
+        issue(it + 2, it & 1, false);
+        issue(it + 1, (it + 1) & 1, true);
+        wait_vmcnt<2 * D>();  // K(it + 1) and V(it) have landed
+      } else {
+        issue(it + 1, (it + 1) & 1, true);
+        wait_vmcnt<D>();
+      }
+      f32x4 pn[C::kBlocks];
+      bool gn;
+      const float an = scores_softmax(it + 1, pn, gn);
+      tile_pv<KV, C::kBlocks>(st, tiles + (2 * (it & 1) + 1) * C::kTileBytes, p);
+      if (gn) {
+#pragma unroll
+        for (int d = 0; d < 16; ++d) st.o[d] *= an;
+      }
+#pragma unroll
+      for (int mb = 0; mb < C::kBlocks; ++mb) p[mb] = pn[mb];
+    }
+    wait_vmcnt<0>();
+    tile_pv<KV, C::kBlocks>(st, tiles + (2 * ((ntiles - 1) & 1) + 1) * C::kTileBytes, p);
   }
 
   const float lrow = group4_sum(st.l);
