@@ -211,18 +211,34 @@ __device__ __forceinline__ void tile_softmax(WaveState& st, f32x4 (&s)[NMB], flo
   st.l += sum;
 }
 
-// O^T += V^T * P^T over the tile's 16 * NMB keys (32-key MFMA steps; a
-// 16-key BF16 tile takes one 16-key step).
+// O^T += V^T * P^T over one tile, in two steps: fetch() requests every V
+// fragment of the tile from LDS, multiply() runs the products, so a caller can
+// place other work (the next tile's scores and softmax) between the requests
+// and the products.  Two tile shapes: 16 BF16 keys (one 16-key step, P as a
+// bf16 high and low part) and 32 FP8 keys (one 32-key step, fp16 P, V widened
+// exactly to fp16).
 template <int KV, int NMB>
-__device__ __forceinline__ void tile_pv(WaveState& st, const lds_t* vt, const f32x4 (&p)[NMB]) {
-  if constexpr (KV == kBF16 && NMB == 1) {
-    // P^T as the B operand: lane holds keys 4 (lane / 16) + j of its row, as
-    // the scores lie.  V^T: transpose-read source lane sl = 4e + q points at
-    // key 4 (lane / 16) + e, columns 4q .. 4q + 3 of the d-block.
-    using G = TileGeom<KV>;
+struct TilePV;
+
+template <>
+struct TilePV<kBF16, 1> {
+  i16x4 a[16];
+  // V^T: transpose-read source lane sl = 4e + q points at key 4 (lane / 16) + e,
+  // columns 4q .. 4q + 3 of the d-block.
+  __device__ __forceinline__ void fetch(const lds_t* vt) {
+    using G = TileGeom<kBF16>;
     const int lane = lane_id();
     const int gq = lane >> 4, sl = lane & 15;
     const int e = sl >> 2, q = sl & 3;
+#pragma unroll
+    for (int mb = 0; mb < 16; ++mb)
+      a[mb] = __builtin_bit_cast(i16x4, lds_tr16(vt + G::off(4 * gq + e, 2 * mb + (q >> 1)) + 8 * (q & 1)));
+  }
+  // P^T as the B operand: lane holds keys 4 (lane / 16) + j of its row, as the
+  // scores lie.  The high parts of all 16 blocks, then the low parts (the same
+  // sums per block as high-then-low, without a product waiting on the one just
+  // before it).
+  __device__ __forceinline__ void multiply(WaveState& st, const f32x4 (&p)[1]) const {
     i16x4 ph, pl;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -231,65 +247,33 @@ __device__ __forceinline__ void tile_pv(WaveState& st, const lds_t* vt, const f3
       ph[j] = __builtin_bit_cast(short, h);
       pl[j] = __builtin_bit_cast(short, (__bf16)(x - (float)h));
     }
-    // Every V fragment first, then the high parts of all 16 blocks and the
-    // low parts (the same sums per block as high-then-low, without a product
-    // waiting on the one just before it).
-    i16x4 a[16];
-#pragma unroll
-    for (int mb = 0; mb < 16; ++mb)
-      a[mb] = __builtin_bit_cast(i16x4, lds_tr16(vt + G::off(4 * gq + e, 2 * mb + (q >> 1)) + 8 * (q & 1)));
-    __builtin_amdgcn_sched_barrier(0);  // keep the requests ahead of the products
 #pragma unroll
     for (int mb = 0; mb < 16; ++mb) st.o[mb] = mfma_bf16_k16(a[mb], ph, st.o[mb]);
 #pragma unroll
     for (int mb = 0; mb < 16; ++mb) st.o[mb] = mfma_bf16_k16(a[mb], pl, st.o[mb]);
-    return;
   }
-  static_assert(NMB % 2 == 0 || (KV == kBF16 && NMB == 1), "tiles hold a multiple of 32 keys");
-  using G = TileGeom<KV>;
-  const int lane = lane_id();
-  const int gq = lane >> 4, sl = lane & 15;
+};
+
+template <>
+struct TilePV<kFP8, 2> {
+  i32x2 raw[16];
+  // Transpose-read source: lane sl = 2e + q points at key(e), bytes 8q .. 8q + 7 of the d-block.
+  __device__ __forceinline__ void fetch(const lds_t* vt) {
+    using G = TileGeom<kFP8>;
+    const int lane = lane_id();
+    const int gq = lane >> 4, sl = lane & 15;
+    const int e = sl >> 1, q = sl & 1;
+    const int key = 16 * (e >> 2) + 4 * gq + (e & 3);
 #pragma unroll
-  for (int t = 0; t < NMB / 2; ++t) {
-    if constexpr (KV == kFP8) {
-      const f16x8 pb = {(_Float16)p[2 * t][0], (_Float16)p[2 * t][1], (_Float16)p[2 * t][2], (_Float16)p[2 * t][3],
-                        (_Float16)p[2 * t + 1][0], (_Float16)p[2 * t + 1][1], (_Float16)p[2 * t + 1][2],
-                        (_Float16)p[2 * t + 1][3]};
-      // transpose-read source: lane sl = 2e + q points at key(e), bytes 8q..8q+7 of the d-block
-      const int e = sl >> 1, q = sl & 1;
-      const int key = 32 * t + 16 * (e >> 2) + 4 * gq + (e & 3);
-      // Every V fragment of the 32-key step is requested before the first product.
-      i32x2 raw[16];
-#pragma unroll
-      for (int mb = 0; mb < 16; ++mb) raw[mb] = lds_tr8(vt + G::off(key, mb) + 8 * q);
-      __builtin_amdgcn_sched_barrier(0);  // keep the requests ahead of the products
-#pragma unroll
-      for (int mb = 0; mb < 16; ++mb) st.o[mb] = mfma_f16(fp8x8_to_f16(raw[mb]), pb, st.o[mb]);
-    } else {
-      bf16x8 ph, pl;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float x = p[2 * t + (j >> 2)][j & 3];
-        const __bf16 h = (__bf16)x;
-        ph[j] = h;
-        pl[j] = (__bf16)(x - (float)h);
-      }
-      // transpose-read source: lane sl = 4e + q points at key(e), columns 4q..4q+3
-      const int e = sl >> 2, q = sl & 3;
-#pragma unroll
-      for (int mb = 0; mb < 16; ++mb) {
-        const int chunk = 2 * mb + (q >> 1);
-        const int key0 = 32 * t + 4 * gq + e;
-        const int key1 = key0 + 16;
-        const i32x2 lo = __builtin_bit_cast(i32x2, lds_tr16(vt + G::off(key0, chunk) + 8 * (q & 1)));
-        const i32x2 hi = __builtin_bit_cast(i32x2, lds_tr16(vt + G::off(key1, chunk) + 8 * (q & 1)));
-        const bf16x8 a = __builtin_bit_cast(bf16x8, i32x4{lo[0], lo[1], hi[0], hi[1]});
-        st.o[mb] = mfma_bf16(a, ph, st.o[mb]);
-        st.o[mb] = mfma_bf16(a, pl, st.o[mb]);
-      }
-    }
+    for (int mb = 0; mb < 16; ++mb) raw[mb] = lds_tr8(vt + G::off(key, mb) + 8 * q);
   }
-}
+  __device__ __forceinline__ void multiply(WaveState& st, const f32x4 (&p)[2]) const {
+    const f16x8 pb = {(_Float16)p[0][0], (_Float16)p[0][1], (_Float16)p[0][2], (_Float16)p[0][3],
+                      (_Float16)p[1][0], (_Float16)p[1][1], (_Float16)p[1][2], (_Float16)p[1][3]};
+#pragma unroll
+    for (int mb = 0; mb < 16; ++mb) st.o[mb] = mfma_f16(fp8x8_to_f16(raw[mb]), pb, st.o[mb]);
+  }
+};
 
 // Several 16-row blocks of one wave on the same tile (FP8 queries and keys,
 // FP8 V): each K fragment read from LDS and each V fragment widened to fp16

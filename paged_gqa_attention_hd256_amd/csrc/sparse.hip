@@ -235,10 +235,12 @@ void sparse_kernel(SparseArgs a) {
         issue(it + 1, (it + 1) & 1, true);
         wait_vmcnt<D>();
       }
+      TilePV<KV, C::kBlocks> pv;
+      pv.fetch(tiles + (2 * (it & 1) + 1) * C::kTileBytes);
       f32x4 pn[C::kBlocks];
       bool gn;
       const float an = scores_softmax(it + 1, pn, gn);
-      tile_pv<KV, C::kBlocks>(st, tiles + (2 * (it & 1) + 1) * C::kTileBytes, p);
+      pv.multiply(st, p);
       if (gn) {
 #pragma unroll
         for (int d = 0; d < 16; ++d) st.o[d] *= an;
@@ -247,7 +249,9 @@ void sparse_kernel(SparseArgs a) {
       for (int mb = 0; mb < C::kBlocks; ++mb) p[mb] = pn[mb];
     }
     wait_vmcnt<0>();
-    tile_pv<KV, C::kBlocks>(st, tiles + (2 * ((ntiles - 1) & 1) + 1) * C::kTileBytes, p);
+    TilePV<KV, C::kBlocks> pv;
+    pv.fetch(tiles + (2 * ((ntiles - 1) & 1) + 1) * C::kTileBytes);
+    pv.multiply(st, p);
   }
 
   const float lrow = group4_sum(st.l);
