@@ -153,17 +153,28 @@ void sparse_kernel(SparseArgs a) {
   for (int c0 = sp * a.split_len; c0 < e_end; c0 += kSparseTableEntries) {
     const int cnt = min(kSparseTableEntries, e_end - c0);
     const int ntiles = (cnt + C::kTileKeys - 1) / C::kTileKeys;
-    // Translate this chunk's entries (and pad the last tile) into physical rows.
-    for (int e = lane; e < ntiles * C::kTileKeys; e += 64) {
-      int phys = -1;
-      if (e < cnt) {
-        const int j = idx_row[c0 + e];
-        if (j >= 0 && j < lk) {
-          const int page = bt_row[j >> a.kv.page_shift];
-          if (page >= 0 && page < a.kv.num_pages) phys = page * a.kv.page_size + (j & pmask);
-        }
-      }
-      lds_store<int>(table + 4 * e, phys);
+    // Translate this chunk's entries (and pad the last tile) into physical
+    // rows: every index of the lane first, then every block-table entry they
+    // need, so the chunk costs two memory round trips rather than two per entry.
+    constexpr int kPer = kSparseTableEntries / 64;  // entries per lane
+    const int nent = ntiles * C::kTileKeys;
+    int jv[kPer], pgv[kPer];
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int e = lane + 64 * k;
+      jv[k] = e < cnt ? idx_row[c0 + e] : -1;
+    }
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int j = jv[k];
+      pgv[k] = (j >= 0 && j < lk) ? bt_row[j >> a.kv.page_shift] : -1;
+    }
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int e = lane + 64 * k;
+      const int j = jv[k], page = pgv[k];
+      const bool ok = j >= 0 && j < lk && page >= 0 && page < a.kv.num_pages;
+      if (e < nent) lds_store<int>(table + 4 * e, ok ? page * a.kv.page_size + (j & pmask) : -1);
     }
 
     // Copies of one operand (K or V) of tile it into stage buf.
