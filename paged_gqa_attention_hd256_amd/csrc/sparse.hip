@@ -169,12 +169,30 @@ void sparse_kernel(SparseArgs a) {
       const int j = jv[k];
       pgv[k] = (j >= 0 && j < lk) ? bt_row[j >> a.kv.page_shift] : -1;
     }
+    // An entry that selects nothing (padding, out of range, the last tile's
+    // tail) is stored negative, which masks its key.  On an evenly spaced pool
+    // it also carries, in its low 31 bits, the row of the chunk's first valid
+    // entry, so its copy reads finite data of the same list (the mask gives it
+    // probability 0 exactly) and the copies need no per-lane fallback address;
+    // a chunk without any valid entry is skipped.
+    int physv[kPer];
+    uint64_t anyv = 0;
+    int first_valid = 0;
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int j = jv[k], page = pgv[k];
+      const bool ok = j >= 0 && j < lk && page >= 0 && page < a.kv.num_pages;
+      physv[k] = ok ? page * a.kv.page_size + (j & pmask) : -1;
+      const uint64_t m = __builtin_amdgcn_ballot_w64(ok);
+      if (anyv == 0 && m != 0) first_valid = __builtin_amdgcn_readlane(physv[k], __builtin_ctzll(m));
+      anyv |= m;
+    }
+    if (anyv == 0) continue;  // nothing selected in this chunk (wave-uniform)
 #pragma unroll
     for (int k = 0; k < kPer; ++k) {
       const int e = lane + 64 * k;
-      const int j = jv[k], page = pgv[k];
-      const bool ok = j >= 0 && j < lk && page >= 0 && page < a.kv.num_pages;
-      if (e < nent) lds_store<int>(table + 4 * e, ok ? page * a.kv.page_size + (j & pmask) : -1);
+      const int ph = physv[k] >= 0 ? physv[k] : (DENSE ? (int)(0x80000000u | (unsigned)first_valid) : -1);
+      if (e < nent) lds_store<int>(table + 4 * e, ph);
     }
 
     // Copies of one operand (K or V) of tile it into stage buf.
@@ -191,7 +209,7 @@ void sparse_kernel(SparseArgs a) {
         const int phys = physv[u];
         uint64_t src;
         if constexpr (DENSE) {
-          src = phys >= 0 ? (uint64_t)(uint32_t)phys * (is_v ? vst : kst) + (is_v ? vb[u] : kb[u]) : zaddr;
+          src = (uint64_t)((uint32_t)phys & 0x7FFFFFFFu) * (is_v ? vst : kst) + (is_v ? vb[u] : kb[u]);
         } else {
           const int row = row0 + lane / G::kChunks;
           const int chunk = (lane % G::kChunks) ^ (row & (G::kChunks - 1));
