@@ -195,6 +195,31 @@ def test_sparse_split_index_handling_bit_exact(kv_dtype):
         assert np.array_equal(bf16_bits_to_f64(bits[t]), expect)
 
 
+@pytest.mark.parametrize("kv_dtype", [w.BF16, w.FP8])
+@pytest.mark.parametrize("stage", ["all", "unsplit"])
+def test_sparse_one_valid_entry_across_chunks(kv_dtype, stage):
+    """Lists of 2,100 entries (three 1,024-entry chunks) with one valid entry in
+    the first, middle or last chunk (or at a chunk edge) on a NaN-poisoned
+    pool: chunks without a valid entry contribute nothing, entries that select
+    nothing never read an unselected row, and the row is RNE(v_ds * V_j)
+    bitwise, split or not."""
+    p = w.poison_unused(w.make_sparse("one_of_2100", [56], [8], [6000], 24, 2, 1, kv_dtype=kv_dtype, width=2100))
+    if kv_dtype == w.FP8:
+        p.v_descale = 0.25
+    cols = [0, 1023, 1024, 1500, 2047, 2048, 2099, 700]
+    for t in range(8):
+        j = p.indices[t, 0]
+        p.indices[t, :] = -1
+        p.indices[t, cols[t]] = j
+    p = w.poison_unused(p)
+    bits, _ = run_gpu(p, stage=stage)
+    _, v = refs.logical_kv(p, 0)
+    for t in range(8):
+        j = p.indices[t][p.indices[t] >= 0][0]
+        expect = refs.bf16_round(np.repeat(v[j].numpy(), 12, axis=0))
+        assert np.array_equal(bf16_bits_to_f64(bits[t]), expect), (t, cols[t])
+
+
 # --------------------------------------------------- determinism, permutation ---
 @pytest.mark.parametrize("mode", ["verify", "prefill", "sparse"])
 def test_bitwise_determinism_and_page_permutation_invariance(mode):
