@@ -71,7 +71,11 @@ __device__ __forceinline__ int2 first_pages(const KvArgs& kv, const int32_t* bt_
   return int2{k_hi > k_lo ? scalar_load(bt_row + p0) : 0, k_hi > k_lo + 64 ? scalar_load(bt_row + p1) : 0};
 }
 
-template <int KV, int NW, class Tile>
+// STREAM: the keys are read exactly once (speculative verify, where each
+// piece of each history belongs to one workgroup), so their copies use the
+// non-temporal cache policy; the prefill re-reads every key from L2 for each
+// query tile and keeps the default policy.
+template <bool STREAM, int KV, int NW, class Tile>
 __device__ __forceinline__ void stream_keys(CausalSmem<KV, NW>& sm, const KvArgs& kv, const int32_t* bt_row, int g,
                                             int k_lo, int k_hi, int2 first, const Tile& tile) {
   using G = TileGeom<KV>;
@@ -117,12 +121,12 @@ __device__ __forceinline__ void stream_keys(CausalSmem<KV, NW>& sm, const KvArgs
                                    : (uint64_t)(uintptr_t)g_zero16;
     if (!page_ok) {
 #pragma unroll
-      for (int u = 0; u < kDma; ++u) dma16_off(pbase, 0u, dst + (kRowsPerWave * w + u * kRowsPerDma) * G::kRowBytes);
+      for (int u = 0; u < kDma; ++u) dma16_off<STREAM>(pbase, 0u, dst + (kRowsPerWave * w + u * kRowsPerDma) * G::kRowBytes);
     } else if (tb + 64 <= k_hi) {  // every key of the tile exists
       const uint64_t tbase = pbase + (uint64_t)((tb & pmask) * (unsigned)st);
 #pragma unroll
       for (int u = 0; u < kDma; ++u)
-        dma16_off(tbase, lane_off[u], dst + (kRowsPerWave * w + u * kRowsPerDma) * G::kRowBytes);
+        dma16_off<STREAM>(tbase, lane_off[u], dst + (kRowsPerWave * w + u * kRowsPerDma) * G::kRowBytes);
     } else {
 #pragma unroll
       for (int u = 0; u < kDma; ++u) {
@@ -130,7 +134,7 @@ __device__ __forceinline__ void stream_keys(CausalSmem<KV, NW>& sm, const KvArgs
         const int row = row0 + lane / G::kChunks;
         const unsigned chunk = (lane % G::kChunks) ^ (row & (G::kChunks - 1));
         const unsigned key = (unsigned)min(tb + row, k_hi - 1);
-        dma16_off(pbase, (key & pmask) * (unsigned)st + chunk * 16, dst + row0 * G::kRowBytes);
+        dma16_off<STREAM>(pbase, (key & pmask) * (unsigned)st + chunk * 16, dst + row0 * G::kRowBytes);
       }
     }
   };

@@ -92,16 +92,29 @@ __device__ __forceinline__ void dma16(const void* src, lds_t* lds_wave_base) {
 }
 // The same copy from a wave-uniform 64-bit base plus a 32-bit per-lane byte
 // offset (the scalar-base form: no 64-bit address arithmetic per lane).
-// `lds_addr` is the wave-uniform LDS byte address lane 0 writes.
+// `lds_addr` is the wave-uniform LDS byte address lane 0 writes.  NT: the load
+// carries the non-temporal cache policy, for data read exactly once (a
+// speculative-verify KV stream): its lines do not displace reused ones.
+template <bool NT = false>
 __device__ __forceinline__ void dma16_off(uint64_t uniform_base, unsigned offset, unsigned lds_addr) {
   const unsigned lds = __builtin_amdgcn_readfirstlane(lds_addr);
-  asm volatile(
-      "s_mov_b32 m0, %2\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %0, %1"
-      :
-      : "v"(offset), "s"(uniform_base), "s"(lds)
-      : "memory", "m0");
+  if constexpr (NT) {
+    asm volatile(
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %0, %1 nt"
+        :
+        : "v"(offset), "s"(uniform_base), "s"(lds)
+        : "memory", "m0");
+  } else {
+    asm volatile(
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %0, %1"
+        :
+        : "v"(offset), "s"(uniform_base), "s"(lds)
+        : "memory", "m0");
+  }
 }
 
 template <class T>

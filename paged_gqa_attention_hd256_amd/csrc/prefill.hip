@@ -54,7 +54,7 @@ __global__ __launch_bounds__(64 * NW, KV == kFP8 ? 2 : 1) void prefill_kernel(Pr
 #pragma unroll
   for (int i = 0; i < 16; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   f32x4 lsum = {0.f, 0.f, 0.f, 0.f};
-  stream_keys(sm, a.kv, bt_row, g, 0, k_hi, first,
+  stream_keys<false>(sm, a.kv, bt_row, g, 0, k_hi, first,
               SplitTile<QDT, KV, NW>{qf, c2 * qf.rscale, klim, min_lim, live, rs, o, lsum, sm.x});
   const float lrow = finish_rows(lsum, live, sm.x);
   if (row_ok && (lane >> 4) == 0 && a.lse)

@@ -192,7 +192,7 @@ __global__ __launch_bounds__(256, (KV == kFP8) ? 2 : 1) void verify_kernel(Verif
 #pragma unroll
     for (int i = 0; i < 16; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
     f32x4 lsum = {0.f, 0.f, 0.f, 0.f};
-    stream_keys(sm, a.kv, bt_row, g, k_lo, k_hi, first,
+    stream_keys<true>(sm, a.kv, bt_row, g, k_lo, k_hi, first,
                 SplitTile<kBF16, KV, 4>{qf, c2 * qf.rscale, klim, min_lim, live, rs, o, lsum, sm.x});
     const float lrow = finish_rows(lsum, live, sm.x);
     // A run that covers a whole uncut unit writes the output; any other piece
