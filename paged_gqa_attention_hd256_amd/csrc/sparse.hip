@@ -162,7 +162,9 @@ void sparse_kernel(SparseArgs a) {
 #pragma unroll
     for (int k = 0; k < kPer; ++k) {
       const int e = lane + 64 * k;
-      jv[k] = e < cnt ? idx_row[c0 + e] : -1;
+      // Each row's list is read exactly once: non-temporal, so it does not
+      // displace the K/V rows that other rows of the sequence reuse from L2.
+      jv[k] = e < cnt ? __builtin_nontemporal_load(idx_row + c0 + e) : -1;
     }
 #pragma unroll
     for (int k = 0; k < kPer; ++k) {
