@@ -160,56 +160,13 @@ __device__ __forceinline__ void tile_scores(const lds_t* kt, const QFragT<KV>& q
   }
 }
 
-// Online-softmax update with the tile's scores; returns the probabilities in
-// s (in place).  `c2` is this row's log2-domain score multiplier.  With
-// MASKED, `visible(key)` (key relative to the tile start) decides which of this
-// lane's keys count.
-//
-// The probabilities are taken relative to a reference maximum m that is only
-// raised when some row's tile maximum exceeds it by more than kRescaleLog2, so
-// the accumulators are rescaled a handful of times per row instead of once per
-// tile; p stays below 2^kRescaleLog2, well inside fp16 and bf16 range, and the
-// row sum l is kept relative to the same reference.
+// Online softmax (every kernel): the probabilities are taken relative to a
+// reference maximum m that is only raised when some row's tile maximum exceeds
+// it by more than kRescaleLog2, so the accumulators are rescaled a handful of
+// times per row instead of once per tile; p stays below 2^kRescaleLog2, well
+// inside fp16 and bf16 range, and the row sum l is kept relative to the same
+// reference.
 constexpr float kRescaleLog2 = 8.0f;
-
-template <bool MASKED, int NMB, class Vis>
-__device__ __forceinline__ void tile_softmax(WaveState& st, f32x4 (&s)[NMB], float c2, Vis visible) {
-  const int gq = lane_id() >> 4;
-  float mt = kNegInf;
-#pragma unroll
-  for (int mb = 0; mb < NMB; ++mb) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float x = s[mb][i] * c2;
-      if constexpr (MASKED) x = visible(mb * 16 + 4 * gq + i) ? x : kNegInf;
-      s[mb][i] = x;
-      mt = fmaxf(mt, x);
-    }
-  }
-  mt = group4_max(mt);
-  if (__builtin_amdgcn_ballot_w64(mt > st.m + kRescaleLog2) != 0) {  // wave-uniform
-    const float m_new = fmaxf(st.m, mt);
-    // 0 when st.m is -inf and the row now has a key; 1 when its maximum did not
-    // move (also a row with no visible key yet, where the difference is NaN).
-    const float alpha = m_new == st.m ? 1.f : fast_exp2(st.m - m_new);
-    st.l *= alpha;
-#pragma unroll
-    for (int d = 0; d < 16; ++d) st.o[d] *= alpha;
-    st.m = m_new;
-  }
-  const float m_use = (st.m == kNegInf) ? 0.f : st.m;
-  float sum = 0.f;
-#pragma unroll
-  for (int mb = 0; mb < NMB; ++mb) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float p = fast_exp2(s[mb][i] - m_use);
-      s[mb][i] = p;
-      sum += p;
-    }
-  }
-  st.l += sum;
-}
 
 // O^T += V^T * P^T over one tile, in two steps: fetch() requests every V
 // fragment of the tile from LDS, multiply() runs the products, so a caller can
@@ -275,10 +232,9 @@ struct TilePV<kFP8, 2> {
   }
 };
 
-// Several 16-row blocks of one wave on the same tile (FP8 queries and keys,
-// FP8 V): each K fragment read from LDS and each V fragment widened to fp16
-// feeds one MFMA per row block, so the LDS reads and the conversions of a tile
-// are shared by NRB * 16 query rows.
+// Scores of several 16-row blocks of one wave on the same tile (FP8 queries
+// and keys): each K fragment read from LDS feeds one MFMA per row block, so
+// the LDS reads of a tile are shared by NRB * 16 query rows.
 template <int NRB, int NMB>
 __device__ __forceinline__ void tile_scores_rows(const lds_t* kt, const QFragT<kFP8> (&qf)[NRB],
                                                  f32x4 (&s)[NRB][NMB]) {
@@ -299,103 +255,6 @@ __device__ __forceinline__ void tile_scores_rows(const lds_t* kt, const QFragT<k
       const i32x8 a = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
 #pragma unroll
       for (int rb = 0; rb < NRB; ++rb) s[rb][mb] = mfma_fp8_scaled(a, qf[rb].hi[h], s[rb][mb], kScaleOne);
-    }
-  }
-}
-
-// Scaled (log2-domain) scores of NRB row blocks, in place.  MASKED: key
-// (relative to the tile start) is visible to a row iff key <= lim[rb]; other
-// keys get -inf.  Only the scores pass through this branch.
-template <bool MASKED, int NRB, int NMB>
-__device__ __forceinline__ void scale_scores_rows(f32x4 (&s)[NRB][NMB], float c2, const int (&lim)[NRB]) {
-  const int gq = lane_id() >> 4;
-#pragma unroll
-  for (int rb = 0; rb < NRB; ++rb)
-#pragma unroll
-    for (int mb = 0; mb < NMB; ++mb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float x = s[rb][mb][i] * c2;
-        s[rb][mb][i] = (!MASKED || mb * 16 + 4 * gq + i <= lim[rb]) ? x : kNegInf;
-      }
-}
-
-// Online-softmax update of NRB row blocks with scaled scores (as tile_softmax),
-// with one wave-uniform rescale decision for all of them, so the accumulators
-// pass through a single branch per tile.  A row whose maximum does not move
-// keeps alpha = 1 (also a row that has seen no visible key yet).
-template <int NRB, int NMB>
-__device__ __forceinline__ void softmax_rows(WaveState (&st)[NRB], f32x4 (&s)[NRB][NMB]) {
-  float mt[NRB];
-  bool grow = false;
-#pragma unroll
-  for (int rb = 0; rb < NRB; ++rb) {
-    float m = kNegInf;
-#pragma unroll
-    for (int mb = 0; mb < NMB; ++mb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) m = fmaxf(m, s[rb][mb][i]);
-    mt[rb] = group4_max(m);
-    grow |= mt[rb] > st[rb].m + kRescaleLog2;
-  }
-  if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-    // The accumulators live in the accumulation registers; this empty asm
-    // redefines them there at the branch entry, so the compiler keeps the
-    // copies to ordinary registers for the multiply inside this (rarely taken)
-    // branch instead of hoisting them into every tile.
-#pragma unroll
-    for (int rb = 0; rb < NRB; ++rb)
-#pragma unroll
-      for (int d = 0; d < 16; ++d) asm volatile("" : "+a"(st[rb].o[d]));
-#pragma unroll
-    for (int rb = 0; rb < NRB; ++rb) {
-      const float m_new = fmaxf(st[rb].m, mt[rb]);
-      const float alpha = m_new == st[rb].m ? 1.f : fast_exp2(st[rb].m - m_new);
-      st[rb].l *= alpha;
-#pragma unroll
-      for (int d = 0; d < 16; ++d) st[rb].o[d] *= alpha;
-      st[rb].m = m_new;
-    }
-  }
-#pragma unroll
-  for (int rb = 0; rb < NRB; ++rb) {
-    const float m_use = (st[rb].m == kNegInf) ? 0.f : st[rb].m;
-    float sum = 0.f;
-#pragma unroll
-    for (int mb = 0; mb < NMB; ++mb) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float p = fast_exp2(s[rb][mb][i] - m_use);
-        s[rb][mb][i] = p;
-        sum += p;
-      }
-    }
-    st[rb].l += sum;
-  }
-}
-
-template <int NRB, int NMB>
-__device__ __forceinline__ void tile_pv_rows(WaveState (&st)[NRB], const lds_t* vt, const f32x4 (&p)[NRB][NMB]) {
-  static_assert(NMB % 2 == 0, "tiles hold a multiple of 32 keys");
-  using G = TileGeom<kFP8>;
-  const int lane = lane_id();
-  const int gq = lane >> 4, sl = lane & 15;
-  const int e = sl >> 1, q = sl & 1;
-#pragma unroll
-  for (int t = 0; t < NMB / 2; ++t) {
-    f16x8 pb[NRB];
-#pragma unroll
-    for (int rb = 0; rb < NRB; ++rb)
-      pb[rb] = f16x8{(_Float16)p[rb][2 * t][0],     (_Float16)p[rb][2 * t][1],     (_Float16)p[rb][2 * t][2],
-                     (_Float16)p[rb][2 * t][3],     (_Float16)p[rb][2 * t + 1][0], (_Float16)p[rb][2 * t + 1][1],
-                     (_Float16)p[rb][2 * t + 1][2], (_Float16)p[rb][2 * t + 1][3]};
-    // transpose-read source: lane sl = 2e + q points at key(e), bytes 8q..8q+7 of the d-block
-    const int key = 32 * t + 16 * (e >> 2) + 4 * gq + (e & 3);
-#pragma unroll
-    for (int mb = 0; mb < 16; ++mb) {
-      const f16x8 a = fp8x8_to_f16(lds_tr8(vt + G::off(key, mb) + 8 * q));
-#pragma unroll
-      for (int rb = 0; rb < NRB; ++rb) st[rb].o[mb] = mfma_f16(a, pb[rb], st[rb].o[mb]);
     }
   }
 }

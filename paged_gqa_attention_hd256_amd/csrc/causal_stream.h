@@ -174,10 +174,11 @@ __device__ __forceinline__ void stream_keys(CausalSmem<KV, NW>& sm, const KvArgs
   }
 }
 
-// Softmax of this wave's 16 rows on a tile (scores s from tile_scores), as
-// tile_softmax does it, except that the rescale factor is published for the PV
-// waves instead of being applied, the probabilities go to LDS as PV operands,
-// and the row sums are left to the PV step (see pv_quarter).
+// Online softmax of this wave's 16 rows on a tile (scores s from tile_scores;
+// reference maximum raised only past kRescaleLog2): the rescale factor is
+// published for the PV waves instead of being applied, the probabilities go
+// to LDS as PV operands, and the row sums are left to the PV step (see
+// pv_quarter).
 template <int KV, bool MASKED, class Vis, int NW>
 __device__ __forceinline__ void softmax_publish(RowStat& rs, f32x4 (&s)[4], float c2, Vis visible,
                                                 Exchange<KV, NW>& x, int w) {

@@ -51,8 +51,7 @@ __device__ __forceinline__ int seq_of(const int32_t* cu_q, int num_seqs, int tok
 // this tile's product is added (1 unless the reference maximum moved; `grow`
 // is set, wave-uniformly, when some row's did).  No branch, so it can run
 // between the products of the previous tile.  The reference maximum moves
-// only when a tile's maximum exceeds it by more than kRescaleLog2, as in
-// tile_softmax.
+// only when a tile's maximum exceeds it by more than kRescaleLog2.
 template <int NMB, class Vis>
 __device__ __forceinline__ float softmax_deferred(float& m, float& l, f32x4 (&s)[NMB], float c2, Vis visible,
                                                   bool& grow) {
