@@ -1,6 +1,6 @@
 """CPU checks of the benchmark's bookkeeping: the kernels it attributes times
-and counters to exist in the HIP sources, and the recorded profile data name
-those kernels."""
+and counters to exist in the HIP sources, the recorded profile data name
+those kernels, and the kernel-trace summary picks out the cold calls."""
 from __future__ import annotations
 
 import json
@@ -38,3 +38,28 @@ def test_counter_records_name_the_benchmarked_kernel():
         k = bench.KERNELS[bench.mode_of(config)]
         assert rec["kernel"] == k["main"], f"{config}: counters of {rec['kernel']}, bench times {k['main']}"
         assert rec["hbm_bytes_per_launch"] > 0
+
+
+def test_trace_summary_separates_cold_calls(tmp_path, capsys):
+    """Cold calls are the library kernels that follow an eviction read; the
+    settle, warmup and warm calls have none before them."""
+    rows = [
+        ("void pga::verify_kernel<2>(pga::VerifyArgs)", 0, 100),           # settle / warmup
+        ("void pga::verify_merge_kernel<2>(pga::VerifyArgs)", 110, 120),
+        ("at::native::reduce_kernel<512, 1>(...)", 200, 500),               # eviction read
+        ("void pga::verify_kernel<2>(pga::VerifyArgs)", 510, 640),          # cold
+        ("void pga::verify_merge_kernel<2>(pga::VerifyArgs)", 650, 670),    # cold
+        ("void pga::verify_kernel<2>(pga::VerifyArgs)", 700, 800),          # warm
+        ("void pga::(anonymous namespace)::quant_amax_kernel(pga::QuantArgs)", 900, 905),
+    ]
+    path = tmp_path / "trace.csv"
+    with open(path, "w") as fh:
+        fh.write("Kind,Kernel_Name,Start_Timestamp,End_Timestamp\n")
+        for name, t0, t1 in rows:
+            fh.write(f'KERNEL_DISPATCH,"{name}",{t0},{t1}\n')
+    bench.trace_summary(str(path))
+    out = json.loads(capsys.readouterr().out)
+    v = out["pga::verify_kernel<2>"]
+    assert v["dispatches"] == 3 and v["cold_calls"] == 1 and v["mean_us_cold"] == 0.13
+    assert out["pga::verify_merge_kernel<2>"]["cold_calls"] == 1
+    assert "pga::quant_amax_kernel" in out
