@@ -9,12 +9,14 @@
 //
 // Per wave, the selected entries are processed in chunks: the wave first
 // translates a chunk of the row's index list into physical token rows of the
-// pool (index -> block-table page -> page * page_size + slot, or -1 for
-// padding) and keeps that table in LDS; then it streams 32-key tiles of K and
-// V through a double-buffered LDS region by 16-byte DMA whose per-lane source
-// comes from the table, and runs the shared attention core on each tile.
-// Because the table is read from LDS, no vector-memory load sits between the
-// DMA instructions and their counter can be waited on exactly.
+// pool (index -> block-table page -> page * page_size + slot; negative for an
+// entry that selects nothing) and keeps that table in LDS; then it streams
+// 32-key (FP8) or 16-key (BF16) tiles of K and V through two LDS stages each
+// by 16-byte DMA whose per-lane source comes from the table, software
+// pipelined: the scores and softmax of tile i + 1 run between the requests
+// and the products of tile i's PV.  Because the table is read from LDS, no
+// vector-memory load sits between the DMA instructions and their counter can
+// be waited on exactly.
 #include "causal_stream.h"
 
 namespace pga {
