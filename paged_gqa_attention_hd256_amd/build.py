@@ -24,6 +24,8 @@ FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
     "-Wall", "-Wno-unused-function",
+    # An inline-asm warning (e.g. a reserved register in a clobber list) fails the build.
+    "-Werror=inline-asm",
 ]
 
 

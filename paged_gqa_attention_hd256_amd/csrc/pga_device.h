@@ -80,15 +80,20 @@ __device__ __forceinline__ void barrier_publish() {
 // wave's copies explicitly with wait_vmcnt.  Compiler-generated waits for its
 // own loads stay correct, only more conservative, because the counter retires
 // loads in issue order.
+//
+// The LDS destination travels in M0.  M0 is an input operand of the asm
+// ("{m0}"): the compiler writes it before the statement and knows it is
+// unchanged after, so no reserved register is clobbered behind its back.  On
+// GFX9 an LDS DMA must not issue in the cycle right after an SALU write of
+// M0; the compiler's hazard check cannot see inside the asm, hence the s_nop.
 __device__ __forceinline__ void dma16(const void* src, lds_t* lds_wave_base) {
   const unsigned base = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)lds_wave_base);
   asm volatile(
-      "s_mov_b32 m0, %1\n\t"
       "s_nop 0\n\t"
       "global_load_lds_dwordx4 %0, off"
       :
-      : "v"(src), "s"(base)
-      : "memory", "m0");
+      : "v"(src), "{m0}"(base)
+      : "memory");
 }
 // The same copy from a wave-uniform 64-bit base plus a 32-bit per-lane byte
 // offset (the scalar-base form: no 64-bit address arithmetic per lane).
@@ -100,20 +105,18 @@ __device__ __forceinline__ void dma16_off(uint64_t uniform_base, unsigned offset
   const unsigned lds = __builtin_amdgcn_readfirstlane(lds_addr);
   if constexpr (NT) {
     asm volatile(
-        "s_mov_b32 m0, %2\n\t"
         "s_nop 0\n\t"
         "global_load_lds_dwordx4 %0, %1 nt"
         :
-        : "v"(offset), "s"(uniform_base), "s"(lds)
-        : "memory", "m0");
+        : "v"(offset), "s"(uniform_base), "{m0}"(lds)
+        : "memory");
   } else {
     asm volatile(
-        "s_mov_b32 m0, %2\n\t"
         "s_nop 0\n\t"
         "global_load_lds_dwordx4 %0, %1"
         :
-        : "v"(offset), "s"(uniform_base), "s"(lds)
-        : "memory", "m0");
+        : "v"(offset), "s"(uniform_base), "{m0}"(lds)
+        : "memory");
   }
 }
 
