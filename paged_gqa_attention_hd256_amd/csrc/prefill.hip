@@ -268,6 +268,20 @@ __global__ __launch_bounds__(512, 1) void prefill_ws_kernel(PrefillArgs a) {
   const int t_hi = min(t_lo + a.tile_tokens, lq);
   const int k_hi = lk - lq + t_hi;
   const int rows = a.r * (t_hi - t_lo);
+  if (k_hi <= 0) {
+    // No key is visible to any row of the tile (a sequence with fewer keys than
+    // queries breaks the caller contract): zero rows and lse = -inf, as the
+    // bf16-query kernel gives, without reading the block table.  Uniform exit,
+    // before any barrier.
+    for (int i = threadIdx.x; i < rows * (kHeadDim / 4); i += blockDim.x) {
+      const int rr = i / (kHeadDim / 4), c = i - rr * (kHeadDim / 4);
+      const int t2 = rr / a.r;
+      const int64_t row = (tok0 + t_lo + t2) * (int64_t)a.hq + g * a.r + rr - t2 * a.r;
+      *reinterpret_cast<uint2*>(a.out + row * kHeadDim + 4 * c) = make_uint2(0u, 0u);
+      if (c == 0 && a.lse) a.lse[row] = kNegInf;
+    }
+    return;
+  }
 
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = lane_id();

@@ -5,7 +5,9 @@ Bar: max-abs <= 1e-2 and rel-L2 <= 2e-3 over the bf16 output, lse within
 the physical page permutation.  Cases span several 64-key tiles with ragged
 tails, split and unsplit verify, both pool layouts, page sizes 16 and 64,
 NaN-poisoned pools (any read outside the visible set shows up), and the
-degenerate shapes of each call.
+degenerate shapes of each call.  Every run writes into buffers with
+sentinel-filled guard margins (tests/gpu_util.py), so a store past either
+end of out, lse or the workspace fails the test that made it.
 """
 import numpy as np
 import pytest
@@ -37,6 +39,15 @@ VERIFY_CASES = [
     ("bf16_hnd_page64", dict(seed=[18], lq=[2, 3], lk=[500, 901], hq=16, hkv=2, kv=w.BF16, layout="HND", page=64)),
     ("fp8_nhd_page64", dict(seed=[19], lq=[4], lk=[1300], hq=16, hkv=1, kv=w.FP8, page=64)),
     ("fp8_lk_equals_lq", dict(seed=[20], lq=[4, 1, 3], lk=[4, 1, 3], hq=16, hkv=1, kv=w.FP8)),
+    # the other per-rank GQA shapes: 3:1 and 6:1, q_len 1..4, both KV encodings
+    ("fp8_3to1_q1to4", dict(seed=[22], lq=[1, 2, 3, 4], lk=[300, 1000, 77, 2100], hq=3, hkv=1, kv=w.FP8)),
+    ("bf16_3to1_2kv", dict(seed=[23], lq=[4, 2, 1], lk=[650, 1290, 64], hq=6, hkv=2, kv=w.BF16)),
+    ("fp8_6to1_2kv", dict(seed=[24], lq=[4, 3, 2, 1], lk=[129, 777, 1600, 31], hq=12, hkv=2, kv=w.FP8)),
+    ("bf16_6to1_q1to4", dict(seed=[25], lq=[2, 4, 1, 3], lk=[999, 260, 1500, 48], hq=6, hkv=1, kv=w.BF16)),
+    # long enough that 64-key segments give more than 64 per unit (the merge
+    # then combines its pieces in several batches of 64)
+    ("fp8_long_many_segments", dict(seed=[26], lq=[4, 1], lk=[5000, 4161], hq=16, hkv=1, kv=w.FP8)),
+    ("bf16_long_many_segments", dict(seed=[27], lq=[3], lk=[4500], hq=8, hkv=1, kv=w.BF16)),
 ]
 
 
@@ -75,6 +86,9 @@ PREFILL_CASES = [
     ("bf16_bf16", dict(seed=[34], lq=[70, 3], lk=[70, 200], hq=8, hkv=1, q=w.BF16, kv=w.BF16)),
     ("fp8_hnd_page64", dict(seed=[35], lq=[65], lk=[390], hq=8, hkv=1, q=w.FP8, kv=w.FP8, layout="HND", page=64)),
     ("fp8_pure_causal", dict(seed=[36], lq=[129], lk=[129], hq=8, hkv=1, q=w.FP8, kv=w.FP8)),
+    ("fp8_6to1", dict(seed=[37], lq=[90, 23], lk=[250, 23], hq=6, hkv=1, q=w.FP8, kv=w.FP8)),
+    ("fp8_3to1_2kv", dict(seed=[38], lq=[85], lk=[300], hq=6, hkv=2, q=w.FP8, kv=w.FP8)),
+    ("bf16q_3to1", dict(seed=[39], lq=[40], lk=[140], hq=3, hkv=1, q=w.BF16, kv=w.FP8)),
 ]
 
 
@@ -94,6 +108,11 @@ SPARSE_CASES = [
     ("fp8_16to1", dict(seed=[45], lq=[10], lk=[999], hq=16, hkv=1, n=257, kv=w.FP8)),
     ("bf16_32to1", dict(seed=[46], lq=[7], lk=[1500], hq=32, hkv=1, n=100, kv=w.BF16)),
     ("fp8_hnd_page64", dict(seed=[47], lq=[8], lk=[3000], hq=6, hkv=1, n=400, kv=w.FP8, layout="HND", page=64)),
+    # the other per-rank GQA shapes: 3:1 and 8:1, both KV encodings
+    ("bf16_3to1", dict(seed=[57], lq=[12], lk=[1500], hq=3, hkv=1, n=300, kv=w.BF16)),
+    ("fp8_3to1_2kv", dict(seed=[58], lq=[9, 4], lk=[1100, 2600], hq=6, hkv=2, n=500, kv=w.FP8)),
+    ("bf16_8to1_2kv", dict(seed=[59], lq=[10], lk=[2300], hq=16, hkv=2, n=350, kv=w.BF16)),
+    ("fp8_8to1", dict(seed=[60], lq=[14], lk=[1800], hq=8, hkv=1, n=1100, kv=w.FP8)),
 ]
 
 
@@ -218,6 +237,45 @@ def test_sparse_one_valid_entry_across_chunks(kv_dtype, stage):
         j = p.indices[t][p.indices[t] >= 0][0]
         expect = refs.bf16_round(np.repeat(v[j].numpy(), 12, axis=0))
         assert np.array_equal(bf16_bits_to_f64(bits[t]), expect), (t, cols[t])
+
+
+# ------------------------------------------------------------ lse = NULL ---
+LSE_NULL_CASES = [
+    ("verify_fp8_split", "verify", 64),
+    ("verify_bf16_unsplit", "verify", 0),
+    ("prefill_fp8", "prefill", None),
+    ("prefill_bf16q", "prefill", None),
+    ("sparse_fp8_split", "sparse", None),
+    ("sparse_bf16_unsplit", "sparse", None),
+]
+
+
+@pytest.mark.parametrize("name,mode,split", LSE_NULL_CASES, ids=[c[0] for c in LSE_NULL_CASES])
+def test_lse_null(name, mode, split):
+    """With no lse pointer every kernel skips its lse stores (no write lands
+    in the guard margins around out and the workspace) and out still meets
+    the bar, bitwise equal to the call that writes lse."""
+    if mode == "verify":
+        kv = w.FP8 if "fp8" in name else w.BF16
+        p = w.make_causal(name, [71], [4, 2, 3], [1300, 90, 2100], 16, 1, kv_dtype=kv,
+                          kv_sigma=0.5 if kv == w.FP8 else 1.0, mode="verify")
+    elif mode == "prefill":
+        qd = w.FP8 if name == "prefill_fp8" else w.BF16
+        p = w.make_causal(name, [72], [70, 9], [300, 9], 8, 1, kv_dtype=w.FP8, q_dtype=qd, mode="prefill")
+    else:
+        kv = w.FP8 if "fp8" in name else w.BF16
+        p = w.make_sparse(name, [73], [6], [3000], 24, 2, 900, kv_dtype=kv)
+    p = w.poison_unused(p)
+    stage = "unsplit" if name == "sparse_bf16_unsplit" else "all"
+    if mode == "sparse":
+        import paged_gqa_attention_hd256_amd as pga
+        assert pga.sparse_splits(24, 2, 6, 900) > 1  # "all" takes the split path
+    ref, ref_lse = oracle.attention(p)
+    bits, _ = run_gpu(p, split=split, stage=stage, with_lse=False)
+    assert_parity(bits, None, ref, ref_lse, what=f"{name}/lse=NULL", check_lse=False)
+    bits_lse, lse = run_gpu(p, split=split, stage=stage)
+    assert np.array_equal(bits, bits_lse)
+    assert_parity(bits_lse, lse, ref, ref_lse, what=f"{name}/with lse")
 
 
 # --------------------------------------------------- determinism, permutation ---
