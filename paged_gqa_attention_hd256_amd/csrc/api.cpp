@@ -21,8 +21,8 @@ constexpr int kFP8 = PGA_DTYPE_FP8_E4M3;
 constexpr int kHeadDim = PGA_HEAD_DIM;
 constexpr int kMaxRowsPerGroup = 64;   // query rows of one kv group a verify workgroup holds
 constexpr int kTileKeys = 64;          // keys per LDS tile of the causal kernels
-constexpr int kMinTilesPerWg = 4;      // verify: shortest run of tiles one workgroup takes
-constexpr int kMaxVerifyWgs = 1024;    // verify: cap of the persistent grid
+constexpr int kMinTilesPerWg = pga::kVerifyMinTilesPerWg;  // verify: shortest run one workgroup takes
+constexpr int kMaxVerifyWgs = pga::kVerifyMaxWgs;          // verify: cap of the persistent grid
 constexpr int kMaxGridYZ = 65535;
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
@@ -95,16 +95,27 @@ struct VerifyPlan {
 // partial rows and their lse values, then the plan the merge reads: per
 // (sequence, kv head) unit its first tile and first segment in the flattened
 // order, and the tiles per workgroup.
-bool plan_verify(int32_t hq, int32_t hkv, int32_t num_seqs, int32_t max_q_len, int32_t max_kv_len,
-                 int32_t kv_split_tokens, VerifyPlan& p) {
-  if (hq <= 0 || hkv <= 0 || hq % hkv != 0 || num_seqs < 0 || max_q_len < 1 || max_kv_len < 0) return false;
-  if (kv_split_tokens < 0 || kv_split_tokens % kTileKeys != 0) return false;
+// Returns PGA_OK, PGA_ERR_SHAPE (invalid arguments) or PGA_ERR_UNSUPPORTED (the
+// flattened work list or the slot indices would not fit the kernels' int32
+// positions).
+int plan_verify(int32_t hq, int32_t hkv, int32_t num_seqs, int32_t max_q_len, int32_t max_kv_len,
+                int32_t kv_split_tokens, VerifyPlan& p) {
+  if (hq <= 0 || hkv <= 0 || hq % hkv != 0 || num_seqs < 0 || max_q_len < 1 || max_kv_len < 0) return PGA_ERR_SHAPE;
+  if (kv_split_tokens < 0 || kv_split_tokens % kTileKeys != 0) return PGA_ERR_SHAPE;
   const int64_t tiles_bound = cdiv(max_kv_len, kTileKeys);
   p.seg_tiles = kv_split_tokens > 0 ? kv_split_tokens / kTileKeys
                                     : static_cast<int32_t>(std::max<int64_t>(1, tiles_bound));
   p.max_segs = static_cast<int32_t>(std::max<int64_t>(1, cdiv(tiles_bound, p.seg_tiles)));
   p.rows_cap = (hq / hkv) * max_q_len;
   const int64_t units = int64_t(num_seqs) * hkv;
+  // Every list position (tiles plus the start cost of each segment, over all
+  // units, and a workgroup's run end wg * tpw past the total) and every slot
+  // index (segments plus workgroups) is an int32 in the kernels; the per-unit
+  // plan entries are addressed as 2 * units.  Half the int32 range leaves the
+  // run ends their margin.
+  if (units * (tiles_bound + int64_t(pga::kVerifySegStartCost) * p.max_segs) > INT32_MAX / 2 ||
+      units * p.max_segs + kMaxVerifyWgs > INT32_MAX / 2 || 2 * units + 4 > INT32_MAX / 2)
+    return PGA_ERR_UNSUPPORTED;
   p.wg_cap = static_cast<int32_t>(std::min<int64_t>(kMaxVerifyWgs, std::max<int64_t>(1, cdiv(units * tiles_bound, kMinTilesPerWg))));
   if (units > 0 && tiles_bound > 0) {
     const size_t slots = size_t(units) * p.max_segs + p.wg_cap;
@@ -113,7 +124,7 @@ bool plan_verify(int32_t hq, int32_t hkv, int32_t num_seqs, int32_t max_q_len, i
     p.ws_lse_bytes = (slots * p.rows_cap * sizeof(float) + 15) & ~size_t(15);
     p.ws_bytes = p.ws_o_bytes + p.ws_lse_bytes + (size_t(units) * 2 + 4) * sizeof(int32_t);
   }
-  return true;
+  return PGA_OK;
 }
 
 // Compute units of the current device (cached per device; 256 if unknown).
@@ -184,14 +195,14 @@ const char* pga_status_string(int status) {
 size_t paged_attn_verify_workspace_bytes(int32_t num_q_heads, int32_t num_kv_heads, int32_t num_seqs,
                                          int32_t max_q_len, int32_t max_kv_len, int32_t kv_split_tokens) {
   VerifyPlan p;
-  if (!plan_verify(num_q_heads, num_kv_heads, num_seqs, max_q_len, max_kv_len, kv_split_tokens, p)) return 0;
+  if (plan_verify(num_q_heads, num_kv_heads, num_seqs, max_q_len, max_kv_len, kv_split_tokens, p) != PGA_OK) return 0;
   return p.ws_bytes;
 }
 
 int32_t paged_attn_verify_split_tokens(int32_t num_q_heads, int32_t num_kv_heads, int32_t num_seqs,
                                        int32_t max_q_len, int32_t max_kv_len, int32_t kv_split_tokens) {
   VerifyPlan p;
-  if (!plan_verify(num_q_heads, num_kv_heads, num_seqs, max_q_len, max_kv_len, kv_split_tokens, p)) return 0;
+  if (plan_verify(num_q_heads, num_kv_heads, num_seqs, max_q_len, max_kv_len, kv_split_tokens, p) != PGA_OK) return 0;
   return p.seg_tiles * kTileKeys;
 }
 
@@ -212,9 +223,8 @@ static int prepare_verify(const void* q, int32_t q_dtype, const float* q_descale
   if (int64_t(r) * max_q_len > kMaxRowsPerGroup) return PGA_ERR_UNSUPPORTED;
   if (kv_split_tokens < 0 || kv_split_tokens % kTileKeys != 0) return PGA_ERR_SHAPE;
   if (!aligned(q, 16) || !aligned(out, 8) || (lse && !aligned(lse, 4))) return PGA_ERR_UNSUPPORTED;
-  if (!plan_verify(num_q_heads, kv->num_kv_heads, num_seqs, max_q_len, max_kv_len, kv_split_tokens, p))
-    return PGA_ERR_SHAPE;
-  if (int64_t(num_seqs) * kv->num_kv_heads > INT32_MAX / 2) return PGA_ERR_UNSUPPORTED;
+  if (int e = plan_verify(num_q_heads, kv->num_kv_heads, num_seqs, max_q_len, max_kv_len, kv_split_tokens, p))
+    return e;
   if (p.ws_bytes > 0 && (!workspace || workspace_bytes < p.ws_bytes)) return PGA_ERR_WORKSPACE;
   if (p.ws_bytes > 0 && !aligned(workspace, 256)) return PGA_ERR_UNSUPPORTED;
   if (num_seqs == 0 || max_kv_len == 0) {

@@ -23,6 +23,15 @@ struct KvArgs {
   const float* v_ds;
 };
 
+// Speculative verify plan constants, shared by the host plan and the kernels.
+// The work list is every unit's 64-key tiles, each segment preceded by
+// kVerifySegStartCost empty positions (the cost of starting a piece: query
+// reload, pipeline refill, partial write); a workgroup takes a run of at
+// least kVerifyMinTilesPerWg positions.  Positions and slot indices are int32.
+constexpr int kVerifySegStartCost = 3;
+constexpr int kVerifyMinTilesPerWg = 4;
+constexpr int kVerifyMaxWgs = 1024;  // cap of the persistent grid
+
 // Speculative verify: persistent stream-K grid over the key tiles of every
 // (sequence, kv head) unit; see verify.hip.
 struct VerifyArgs {

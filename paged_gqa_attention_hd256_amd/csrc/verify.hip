@@ -25,12 +25,12 @@
 
 namespace pga {
 
-constexpr int kMinTilesPerWg = 4;  // shortest run a workgroup takes (in plan units)
+constexpr int kMinTilesPerWg = kVerifyMinTilesPerWg;  // shortest run a workgroup takes (in plan units)
 // Plan units charged for starting a piece of work: a workgroup that begins a
 // second piece reloads its queries, refills its pipeline and writes a partial
 // result, which costs about as much as streaming this many tiles.  Each
 // segment is preceded by this many units without keys in the flattened list.
-constexpr int kSegStartCost = 3;
+constexpr int kSegStartCost = kVerifySegStartCost;
 
 // Per-sequence work of the plan, per kv head: 64-key tiles, segments, and the
 // length in the flattened list (tiles plus the start cost of each segment).

@@ -41,7 +41,7 @@ def test_library_exports_every_declared_function(lib):
 
 def test_status_strings(lib):
     for code in range(0, 8):
-        assert pga.status_string(code)
+        assert pga.status_string(code) != "unknown status"
     assert pga.status_string(99) == "unknown status"
 
 
@@ -102,6 +102,18 @@ def test_verify_rejects_invalid_arguments(lib):
     assert need > 0
     assert verify(lib, ws=None, wsb=0) == EWS
     assert verify(lib, ws=P(), wsb=need - 1) == EWS
+
+
+def test_verify_rejects_plans_past_int32_positions(lib):
+    # The kernels index the flattened tile list and the workspace slots with
+    # int32 positions: a batch whose list would not fit is refused before any
+    # launch (no workspace is looked at), and the workspace query returns 0.
+    big = dict(nseq=1 << 20, maxk=1 << 20)                  # 2^20 units x 16,384 tiles
+    assert verify(lib, kv=kv_struct(block_table_stride=1 << 16), **big, ws=P(), wsb=1 << 62) == EUNSUP
+    assert pga.verify_workspace_bytes(16, 1, 1 << 20, 4, 1 << 20, 0) == 0
+    assert pga.verify_workspace_bytes(16, 1, 1 << 20, 4, 1 << 20, 64) == 0
+    # just inside: 2^15 sequences x 16,384 tiles + 3 start positions < 2^30
+    assert pga.verify_workspace_bytes(16, 1, 1 << 15, 4, 1 << 20, 0) > 0
 
 
 def test_verify_nothing_to_do_returns_ok_without_launch(lib):
