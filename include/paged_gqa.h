@@ -65,8 +65,10 @@
 extern "C" {
 #endif
 
-#define PGA_ABI_VERSION 3
+#define PGA_ABI_VERSION 4
 #define PGA_HEAD_DIM 256
+/* Bytes of the fixed per-device scratch of paged_attn_verify_noalloc (128 MiB). */
+#define PGA_VERIFY_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
 
 /* Element encodings. */
 enum pga_dtype {
@@ -83,7 +85,8 @@ enum pga_status {
   PGA_ERR_UNSUPPORTED = 4, /* outside the kernel envelope: page size, alignment, rows per group */
   PGA_ERR_WORKSPACE = 5,   /* workspace smaller than the matching *_workspace_bytes() */
   PGA_ERR_LAUNCH = 6,      /* the HIP runtime refused a launch (or a copy / synchronisation failed) */
-  PGA_ERR_INVALID_DATA = 7 /* pga_validate_inputs found device data that breaks a precondition */
+  PGA_ERR_INVALID_DATA = 7, /* pga_validate_inputs found device data that breaks a precondition */
+  PGA_ERR_SCRATCH = 8       /* paged_attn_verify_noalloc: the call needs more than its fixed scratch */
 };
 
 /* The paged KV cache.  K and V share dtype, head count and page size; their
@@ -160,6 +163,32 @@ int paged_attn_verify_merge(const void* q, int32_t q_dtype, const float* q_desca
                             int32_t max_q_len, int32_t max_kv_len, const pga_paged_kv* kv, float softmax_scale,
                             int32_t kv_split_tokens, void* workspace, size_t workspace_bytes, void* out,
                             float* lse, void* stream);
+
+/*
+ * paged_attn_verify without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  It runs the same two kernels as
+ * paged_attn_verify (same arguments and result) with the partial rows, their
+ * lse values and the merge plan in a fixed scratch array of
+ * PGA_VERIFY_NOALLOC_SCRATCH_BYTES that each device the library runs on holds
+ * from the first such call until the process ends.  The call allocates and
+ * frees nothing.  The scratch holds, for units = num_seqs * num_kv_heads,
+ * segs = ceil(ceil(max_kv_len / 64) / (kv_split_tokens / 64)) (1 when
+ * kv_split_tokens is 0), slots = units * segs + the persistent grid (at most
+ * 2 workgroups per compute unit) and rows = (num_q_heads / num_kv_heads) *
+ * max_q_len: slots * rows * 256 partial values (2 bytes each for FP8 V, 4 for
+ * BF16 V) plus slots * rows lse values; a call whose bounds need more returns
+ * PGA_ERR_SCRATCH and launches nothing.  Nothing in the scratch needs to
+ * start at zero: every value the merge reads is written earlier in the same
+ * call.  All calls on one device share that device's scratch, so two calls
+ * that may overlap in time on one device (different streams, different host
+ * threads) race: serialise them.  Returns PGA_OK or a PGA_ERR_* code
+ * (PGA_ERR_LAUNCH also when the scratch's device address cannot be looked up).
+ */
+int paged_attn_verify_noalloc(const void* q, int32_t q_dtype, const float* q_descale, int32_t num_q_heads,
+                              int32_t num_seqs, const int32_t* cu_seqlens_q, const int32_t* seq_lens_k,
+                              int32_t max_q_len, int32_t max_kv_len, const pga_paged_kv* kv, float softmax_scale,
+                              int32_t kv_split_tokens, void* out, float* lse, void* stream);
 
 /* Workspace bytes paged_attn_verify needs for these host bounds.  A balanced
  * split can cut any history, so this is > 0 whenever the bounds admit any

@@ -19,7 +19,7 @@ from typing import Optional
 import torch
 
 __all__ = [
-    "PagedKV", "paged_attn_verify", "paged_attn_prefill_prefix", "sparse_paged_attn", "sparse_splits",
+    "PagedKV", "paged_attn_verify", "paged_attn_verify_noalloc", "paged_attn_prefill_prefix", "sparse_paged_attn", "sparse_splits",
     "sparse_workspace_bytes", "prefill_quantize_fp8", "quantize_workspace_bytes", "validate_inputs",
     "verify_workspace_bytes", "verify_split_tokens", "status_string", "abi_version", "library_path",
     "PagedGQAError", "LibraryNotBuilt", "load_library",
@@ -75,6 +75,8 @@ def load_library():
             for fn in ("paged_attn_verify", "paged_attn_verify_partials", "paged_attn_verify_merge"):
                 getattr(lib, fn).argtypes = [P, I32, P, I32, I32, P, P, I32, I32, KVP, F, I32, P, SZ, P, P, P]
                 getattr(lib, fn).restype = ctypes.c_int
+            lib.paged_attn_verify_noalloc.argtypes = [P, I32, P, I32, I32, P, P, I32, I32, KVP, F, I32, P, P, P]
+            lib.paged_attn_verify_noalloc.restype = ctypes.c_int
             lib.paged_attn_verify_workspace_bytes.argtypes = [I32, I32, I32, I32, I32, I32]
             lib.paged_attn_verify_workspace_bytes.restype = SZ
             lib.paged_attn_verify_split_tokens.argtypes = [I32, I32, I32, I32, I32, I32]
@@ -222,6 +224,23 @@ def paged_attn_verify(q, cu_seqlens_q, seq_lens_k, max_q_len: int, max_kv_len: i
                                0 if workspace is None else workspace.numel() * workspace.element_size(),
                                out.data_ptr(), _ptr(lse), _stream(stream))
     _check(fn, st)
+    return out
+
+
+def paged_attn_verify_noalloc(q, cu_seqlens_q, seq_lens_k, max_q_len: int, max_kv_len: int, kv: PagedKV,
+                              softmax_scale: float, out, kv_split_tokens: int = 0, q_descale=None, lse=None,
+                              stream=None):
+    """paged_attn_verify without a workspace: the library keeps the partials in
+    its fixed per-device scratch (PGA_VERIFY_NOALLOC_SCRATCH_BYTES) and
+    allocates nothing.  ``out`` must be given (this wrapper allocates nothing
+    either).  Calls that may overlap on one device must be serialised."""
+    lib = load_library()
+    s = kv._struct()
+    st = lib.paged_attn_verify_noalloc(q.data_ptr(), _dtype_code(q), _ptr(q_descale), q.shape[1],
+                                       seq_lens_k.shape[0], cu_seqlens_q.data_ptr(), seq_lens_k.data_ptr(),
+                                       max_q_len, max_kv_len, ctypes.byref(s), float(softmax_scale), kv_split_tokens,
+                                       out.data_ptr(), _ptr(lse), _stream(stream))
+    _check("paged_attn_verify_noalloc", st)
     return out
 
 

@@ -188,6 +188,7 @@ const char* pga_status_string(int status) {
     case PGA_ERR_WORKSPACE: return "workspace too small";
     case PGA_ERR_LAUNCH: return "kernel launch failed";
     case PGA_ERR_INVALID_DATA: return "device data break a precondition (see the counts)";
+    case PGA_ERR_SCRATCH: return "the call needs more than the fixed scratch of the allocation-free entry point";
     default: return "unknown status";
   }
 }
@@ -207,11 +208,15 @@ int32_t paged_attn_verify_split_tokens(int32_t num_q_heads, int32_t num_kv_heads
 }
 
 // Validates a verify call and fills the launch arguments; returns a status.
+// With use_scratch the caller's workspace arguments are ignored and the
+// partials go to the library's fixed per-device scratch, laid out for this
+// call exactly (partial rows in their stored width, slots for the actual
+// grid) and refused with PGA_ERR_SCRATCH when they do not fit.
 static int prepare_verify(const void* q, int32_t q_dtype, const float* q_descale, int32_t num_q_heads,
                           int32_t num_seqs, const int32_t* cu_seqlens_q, const int32_t* seq_lens_k, int32_t max_q_len,
                           int32_t max_kv_len, const pga_paged_kv* kv, float softmax_scale, int32_t kv_split_tokens,
                           void* workspace, size_t workspace_bytes, void* out, float* lse, VerifyPlan& p,
-                          pga::VerifyArgs& a, int& num_wg, bool& nothing) {
+                          pga::VerifyArgs& a, int& num_wg, bool& nothing, bool use_scratch = false) {
   nothing = false;
   if (!q || !cu_seqlens_q || !seq_lens_k || !out || !kv) return PGA_ERR_NULL;
   if (num_seqs < 0 || num_q_heads <= 0 || max_kv_len < 0) return PGA_ERR_SHAPE;
@@ -225,12 +230,29 @@ static int prepare_verify(const void* q, int32_t q_dtype, const float* q_descale
   if (!aligned(q, 16) || !aligned(out, 8) || (lse && !aligned(lse, 4))) return PGA_ERR_UNSUPPORTED;
   if (int e = plan_verify(num_q_heads, kv->num_kv_heads, num_seqs, max_q_len, max_kv_len, kv_split_tokens, p))
     return e;
-  if (p.ws_bytes > 0 && (!workspace || workspace_bytes < p.ws_bytes)) return PGA_ERR_WORKSPACE;
-  if (p.ws_bytes > 0 && !aligned(workspace, 256)) return PGA_ERR_UNSUPPORTED;
+  const int occupancy = kv->dtype == kFP8 ? 2 : 1;  // workgroups per CU the LDS allows
+  num_wg = std::max(1, std::min(p.wg_cap, device_cus() * occupancy));
+  size_t ws_o_bytes = p.ws_o_bytes, ws_lse_bytes = p.ws_lse_bytes;
+  if (use_scratch) {
+    if (p.ws_bytes > 0) {
+      const int64_t units = int64_t(num_seqs) * kv->num_kv_heads;
+      const size_t slots = size_t(units) * p.max_segs + size_t(num_wg);
+      const size_t part = kv->dtype == kFP8 ? sizeof(uint16_t) : sizeof(float);  // stored partial width
+      ws_o_bytes = (slots * p.rows_cap * kHeadDim * part + 255) & ~size_t(255);
+      ws_lse_bytes = (slots * p.rows_cap * sizeof(float) + 15) & ~size_t(15);
+      const size_t need = ws_o_bytes + ws_lse_bytes + (size_t(units) * 2 + 4) * sizeof(int32_t);
+      if (need > pga::kVerifyScratchBytes) return PGA_ERR_SCRATCH;
+    }
+    workspace = nullptr;
+  } else {
+    if (p.ws_bytes > 0 && (!workspace || workspace_bytes < p.ws_bytes)) return PGA_ERR_WORKSPACE;
+    if (p.ws_bytes > 0 && !aligned(workspace, 256)) return PGA_ERR_UNSUPPORTED;
+  }
   if (num_seqs == 0 || max_kv_len == 0) {
     nothing = true;
     return PGA_OK;
   }
+  if (use_scratch && pga::verify_scratch(&workspace) != hipSuccess) return PGA_ERR_LAUNCH;
   a = pga::VerifyArgs{};
   a.q = static_cast<const uint16_t*>(q);
   a.q_ds = q_descale;
@@ -248,10 +270,8 @@ static int prepare_verify(const void* q, int32_t q_dtype, const float* q_descale
   a.out = static_cast<uint16_t*>(out);
   a.lse = lse;
   a.ws_o = workspace;
-  a.ws_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + p.ws_o_bytes);
-  a.ws_plan = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + p.ws_o_bytes + p.ws_lse_bytes);
-  const int occupancy = kv->dtype == kFP8 ? 2 : 1;  // workgroups per CU the LDS allows
-  num_wg = std::max(1, std::min(p.wg_cap, device_cus() * occupancy));
+  a.ws_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + ws_o_bytes);
+  a.ws_plan = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + ws_o_bytes + ws_lse_bytes);
   return PGA_OK;
 }
 
@@ -296,6 +316,24 @@ int paged_attn_verify(const void* q, int32_t q_dtype, const float* q_descale, in
   int num_wg = 0;
   bool nothing;
   if (int e = prepare_verify(PGA_VERIFY_ARGS, p, a, num_wg, nothing)) return e;
+  if (nothing) return PGA_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (int e = launch_status(pga::launch_verify(a, kv->dtype, num_wg, s))) return e;
+  return launch_status(pga::launch_verify_merge(a, kv->dtype, num_wg, s));
+}
+
+int paged_attn_verify_noalloc(const void* q, int32_t q_dtype, const float* q_descale, int32_t num_q_heads,
+                              int32_t num_seqs, const int32_t* cu_seqlens_q, const int32_t* seq_lens_k,
+                              int32_t max_q_len, int32_t max_kv_len, const pga_paged_kv* kv, float softmax_scale,
+                              int32_t kv_split_tokens, void* out, float* lse, void* stream) {
+  VerifyPlan p;
+  pga::VerifyArgs a;
+  int num_wg = 0;
+  bool nothing;
+  if (int e = prepare_verify(q, q_dtype, q_descale, num_q_heads, num_seqs, cu_seqlens_q, seq_lens_k, max_q_len,
+                             max_kv_len, kv, softmax_scale, kv_split_tokens, nullptr, 0, out, lse, p, a, num_wg,
+                             nothing, /*use_scratch=*/true))
+    return e;
   if (nothing) return PGA_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (int e = launch_status(pga::launch_verify(a, kv->dtype, num_wg, s))) return e;

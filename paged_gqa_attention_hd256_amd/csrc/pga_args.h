@@ -3,7 +3,10 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <stddef.h>
 #include <stdint.h>
+
+#include "paged_gqa.h"
 
 namespace pga {
 
@@ -127,6 +130,11 @@ struct ValidateArgs {
   int32_t num_selected;
   int32_t* counts;         // [kValidateCounts] device counters
 };
+
+// Allocation-free verify (noalloc.hip): bytes of the fixed per-device scratch,
+// and its device address on the current device (looked up once per device).
+constexpr size_t kVerifyScratchBytes = PGA_VERIFY_NOALLOC_SCRATCH_BYTES;
+hipError_t verify_scratch(void** ptr);
 
 // Launchers (defined next to their kernels).  They return the launch status.
 hipError_t launch_verify(const VerifyArgs& a, int kv_dtype, int num_wg, hipStream_t s);

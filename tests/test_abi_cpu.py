@@ -14,7 +14,7 @@ from paged_gqa_attention_hd256_amd import _KV
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "paged_gqa.h")
 
-OK, ENULL, ESHAPE, EDTYPE, EUNSUP, EWS = 0, 1, 2, 3, 4, 5
+OK, ENULL, ESHAPE, EDTYPE, EUNSUP, EWS, ESCRATCH = 0, 1, 2, 3, 4, 5, 8
 
 
 def declared_functions():
@@ -36,11 +36,11 @@ def test_library_exports_every_declared_function(lib):
     assert {"paged_attn_verify", "paged_attn_prefill_prefix", "sparse_paged_attn"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.pga_abi_version() == 3
+    assert lib.pga_abi_version() == 4
 
 
 def test_status_strings(lib):
-    for code in range(0, 8):
+    for code in range(0, 9):
         assert pga.status_string(code) != "unknown status"
     assert pga.status_string(99) == "unknown status"
 
@@ -114,6 +114,30 @@ def test_verify_rejects_plans_past_int32_positions(lib):
     assert pga.verify_workspace_bytes(16, 1, 1 << 20, 4, 1 << 20, 64) == 0
     # just inside: 2^15 sequences x 16,384 tiles + 3 start positions < 2^30
     assert pga.verify_workspace_bytes(16, 1, 1 << 15, 4, 1 << 20, 0) > 0
+
+
+def verify_noalloc(lib, kv=None, **kw):
+    a = dict(q=P(), q_dtype=1, qds=None, hq=16, nseq=2, cuq=P(16384), lk=P(16384 + 64), maxq=4, maxk=1000,
+             scale=0.0625, split=0, out=P(20000), lse=None)
+    a.update(kw)
+    kv = kv or kv_struct()
+    return lib.paged_attn_verify_noalloc(a["q"], a["q_dtype"], a["qds"], a["hq"], a["nseq"], a["cuq"], a["lk"],
+                                         a["maxq"], a["maxk"], ctypes.byref(kv), a["scale"], a["split"], a["out"],
+                                         a["lse"], None)
+
+
+def test_verify_noalloc_checks_before_touching_the_scratch(lib):
+    # Argument checks are those of paged_attn_verify ...
+    assert verify_noalloc(lib, q=None) == ENULL
+    assert verify_noalloc(lib, q_dtype=2) == EDTYPE
+    assert verify_noalloc(lib, maxq=5) == ESHAPE
+    assert verify_noalloc(lib, hq=32) == EUNSUP
+    assert verify_noalloc(lib, nseq=0) == OK          # nothing to do: no scratch lookup, no launch
+    # ... and bounds whose partials exceed the fixed scratch are refused
+    # before its device address is looked up: 4,096 sequences x 1,024
+    # segments of 64 keys x 64 rows x 256 fp16 values is far past 128 MiB.
+    big = dict(nseq=4096, maxk=65536, split=64)
+    assert verify_noalloc(lib, kv=kv_struct(block_table_stride=4096), **big) == ESCRATCH
 
 
 def test_verify_nothing_to_do_returns_ok_without_launch(lib):
