@@ -263,6 +263,26 @@ size_t sparse_paged_attn_workspace_bytes(int32_t num_q_heads, int32_t num_kv_hea
                                          int32_t num_selected);
 
 /*
+ * Measurement helper, not part of the attention path: the same-index gather
+ * of sparse_paged_attn.  For every query row and kv head it copies exactly
+ * the K and V rows that the row's valid list entries select (the same
+ * index -> block-table page -> pool row translation and the same 16-byte
+ * global-to-LDS copies as the attention kernel) and sums their 32-bit words:
+ *   out[row][g][w] = sum over valid entries j of (word w of K_j[g] + word w
+ *                    of V_j[g]) mod 2^32,  w < 256 * element bytes / 4
+ * Its time prices the gather on its own: the practical bandwidth roof of
+ * the selected-token call on the same selection (vLLM PR #62590, Measured
+ * results: the row counts and selections whose kernel times it reports).
+ * Arguments as in sparse_paged_attn; out is uint32 [num_q_tokens,
+ * num_kv_heads, 64 (FP8) or 128 (BF16)], 16-byte aligned.  The pool must be
+ * evenly spaced (stride_page = page_size * stride_token for K and V) with
+ * every row's byte offset below 2^32; otherwise PGA_ERR_UNSUPPORTED.
+ */
+int sparse_gather_sum(int32_t num_q_tokens, int32_t num_seqs, const int32_t* cu_seqlens_q, const int32_t* seq_lens_k,
+                      const int32_t* indices, int64_t index_stride, int32_t num_selected, const pga_paged_kv* kv,
+                      uint32_t* out, void* stream);
+
+/*
  * Per-tensor FP8 (OCP E4M3FN) quantisation of a prefix-hit prefill's inputs,
  * the step ahead of paged_attn_prefill_prefix with FP8 Q (ROCm/ATOM PR #2534,
  * FMHA commit message and Results: its prefill timings include the casts of

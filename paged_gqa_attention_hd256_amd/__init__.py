@@ -19,8 +19,8 @@ from typing import Optional
 import torch
 
 __all__ = [
-    "PagedKV", "paged_attn_verify", "paged_attn_verify_noalloc", "paged_attn_prefill_prefix", "sparse_paged_attn", "sparse_splits",
-    "sparse_workspace_bytes", "prefill_quantize_fp8", "quantize_workspace_bytes", "validate_inputs",
+    "PagedKV", "paged_attn_verify", "paged_attn_verify_noalloc", "paged_attn_prefill_prefix", "sparse_paged_attn",
+    "sparse_splits", "sparse_gather_sum", "sparse_workspace_bytes", "prefill_quantize_fp8", "quantize_workspace_bytes", "validate_inputs",
     "verify_workspace_bytes", "verify_split_tokens", "status_string", "abi_version", "library_path",
     "PagedGQAError", "LibraryNotBuilt", "load_library",
 ]
@@ -85,6 +85,8 @@ def load_library():
             lib.paged_attn_prefill_prefix.restype = ctypes.c_int
             lib.sparse_paged_attn.argtypes = [P, I32, P, I32, I32, I32, P, P, P, I64, I32, KVP, F, P, SZ, P, P, P]
             lib.sparse_paged_attn.restype = ctypes.c_int
+            lib.sparse_gather_sum.argtypes = [I32, I32, P, P, P, I64, I32, KVP, P, P]
+            lib.sparse_gather_sum.restype = ctypes.c_int
             lib.sparse_paged_attn_splits.argtypes = [I32, I32, I32, I32]
             lib.sparse_paged_attn_splits.restype = I32
             lib.sparse_paged_attn_workspace_bytes.argtypes = [I32, I32, I32, I32]
@@ -291,6 +293,26 @@ def sparse_paged_attn(q, cu_seqlens_q, seq_lens_k, indices, kv: PagedKV, softmax
                                _ptr(workspace), 0 if workspace is None else workspace.numel() * workspace.element_size(),
                                out.data_ptr(), _ptr(lse), _stream(stream))
     _check("sparse_paged_attn", st)
+    return out
+
+
+def sparse_gather_sum(cu_seqlens_q, seq_lens_k, indices, kv: PagedKV, num_selected: Optional[int] = None,
+                      out=None, stream=None):
+    """Measurement helper: the same-index gather of ``sparse_paged_attn``
+    (the K and V rows each row's valid entries select, per kv head), summed
+    as 32-bit words; returns uint32-valued int32 ``out`` [T, Hkv, row words]."""
+    lib = load_library()
+    s = kv._struct()
+    if indices.dtype != torch.int32 or indices.dim() != 2 or indices.stride(1) != 1:
+        raise ValueError("indices must be a row-major int32 [T, W] tensor")
+    ns = indices.shape[1] if num_selected is None else num_selected
+    words = 256 * (1 if s.dtype == FP8 else 2) // 4
+    if out is None:
+        out = torch.empty((indices.shape[0], kv.num_kv_heads, words), dtype=torch.int32, device=indices.device)
+    st = lib.sparse_gather_sum(indices.shape[0], seq_lens_k.shape[0], cu_seqlens_q.data_ptr(), seq_lens_k.data_ptr(),
+                               indices.data_ptr(), indices.stride(0), ns, ctypes.byref(s), out.data_ptr(),
+                               _stream(stream))
+    _check("sparse_gather_sum", st)
     return out
 
 

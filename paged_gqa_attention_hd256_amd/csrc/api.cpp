@@ -433,6 +433,36 @@ int sparse_paged_attn(const void* q, int32_t q_dtype, const float* q_descale, in
   return launch_status(pga::launch_sparse(a, kv->dtype, static_cast<hipStream_t>(stream)));
 }
 
+int sparse_gather_sum(int32_t num_q_tokens, int32_t num_seqs, const int32_t* cu_seqlens_q, const int32_t* seq_lens_k,
+                      const int32_t* indices, int64_t index_stride, int32_t num_selected, const pga_paged_kv* kv,
+                      uint32_t* out, void* stream) {
+  if (!cu_seqlens_q || !seq_lens_k || !out || !kv) return PGA_ERR_NULL;
+  if (num_selected > 0 && !indices) return PGA_ERR_NULL;
+  if (num_seqs < 0 || num_q_tokens < 0 || num_selected < 0 || index_stride < num_selected) return PGA_ERR_SHAPE;
+  if (num_q_tokens > 0 && num_seqs == 0) return PGA_ERR_SHAPE;
+  if (int e = check_kv(kv, kv->num_kv_heads > 0 ? kv->num_kv_heads : 1, -1)) return e;
+  // Evenly spaced token rows, addressed by 32-bit byte offsets from each head's base.
+  if (kv->k_stride_page != int64_t(kv->page_size) * kv->k_stride_token ||
+      kv->v_stride_page != int64_t(kv->page_size) * kv->v_stride_token)
+    return PGA_ERR_UNSUPPORTED;
+  const int64_t rows = int64_t(kv->num_pages) * kv->page_size;
+  const int64_t st = std::max(kv->k_stride_token, kv->v_stride_token) * elt_bytes(kv->dtype);
+  if (rows > INT32_MAX || rows * st + kHeadDim * elt_bytes(kv->dtype) > int64_t(UINT32_MAX)) return PGA_ERR_UNSUPPORTED;
+  if (!aligned(out, 16) || (num_selected > 0 && !aligned(indices, 4))) return PGA_ERR_UNSUPPORTED;
+  if (num_q_tokens == 0) return PGA_OK;
+  pga::GatherArgs a{};
+  a.num_tokens = num_q_tokens;
+  a.num_seqs = num_seqs;
+  a.cu_q = cu_seqlens_q;
+  a.lens_k = seq_lens_k;
+  a.idx = indices;
+  a.idx_stride = index_stride;
+  a.num_selected = num_selected;
+  a.kv = make_kv(kv);
+  a.out = out;
+  return launch_status(pga::launch_gather_sum(a, kv->dtype, static_cast<hipStream_t>(stream)));
+}
+
 size_t sparse_paged_attn_workspace_bytes(int32_t num_q_heads, int32_t num_kv_heads, int32_t num_q_tokens,
                                          int32_t num_selected) {
   SparsePlan p;

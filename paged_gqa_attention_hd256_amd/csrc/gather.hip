@@ -1,0 +1,189 @@
+// Same-index gather of the selected-token call's K and V rows: the practical
+// bandwidth roof of sparse_paged_attn on a given selection (measurement only).
+//
+// The sparse kernel's cost on the pages' workload (vLLM PR #62590, "Tune sparse
+// GQA prefill profile on gfx942 and gfx950": Overview, Measured results -- 2,051
+// selected rows per query row gathered from a pool that the caches hold) is
+// the gather, not the arithmetic.  This kernel moves exactly the rows that
+// call attends, through the same translation (index -> block-table page ->
+// physical row) and the same 16-byte global->LDS copies into the same per-wave
+// tiles, and does nothing with them but sum their 32-bit words, so its rate is
+// what the gather alone reaches on this part.
+//
+// Work unit: one wave per (query row, kv head) -- the rows that every 16-head
+// block of that kv group reads once each in the attention kernel.  Waves are
+// independent (no barriers).  Per chunk of up to 1,024 list entries the wave
+// translates the entries into a table of physical rows in LDS (negative for an
+// entry that selects nothing, carrying the chunk's first valid row so its copy
+// stays in bounds), then streams tiles of K and V rows through two LDS stages,
+// copies of tile i + 1 in flight while tile i is summed.  Only the pool's
+// evenly spaced layout is handled (page stride = page size x token stride for
+// K and for V), the one the benchmarked selections use.
+//
+// Output: out[row][kv head][w] = sum over the row's valid entries j of the
+// 32-bit words w of K_j and of V_j of that head (row bytes / 4 words), mod
+// 2^32 -- an exact, order-independent checksum.
+#include "causal_stream.h"
+
+namespace pga {
+
+typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
+
+template <int KV>
+struct GatherCfg {
+  using G = TileGeom<KV>;
+  static constexpr int kWaves = 4;
+  static constexpr int kTileKeys = (KV == kFP8) ? 32 : 16;                   // rows of one stage (as the sparse kernel)
+  static constexpr int kTileBytes = G::template tile_bytes<kTileKeys>();     // 8 KB
+  static constexpr int kTable = 1024;                                        // list entries translated at a time
+  static constexpr int kWaveBytes = 4 * kTileBytes + 4 * kTable;              // 2 stages x (K, V) + table
+  static constexpr int kRowsPerDma = 1024 / G::kRowBytes;                    // 4 (FP8) or 2 (BF16)
+  static constexpr int kDma = kTileKeys / kRowsPerDma;                       // copies per operand and tile: 8
+};
+
+// Sequence of a query row: the last b with cu_q[b] <= tok.
+__device__ __forceinline__ int gather_seq_of(const int32_t* cu_q, int num_seqs, int tok) {
+  int lo = 0, hi = num_seqs - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (cu_q[mid] <= tok) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+template <int KV>
+__global__ __launch_bounds__(GatherCfg<KV>::kWaves * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void gather_sum_kernel(GatherArgs a) {
+  using C = GatherCfg<KV>;
+  using G = typename C::G;
+  __shared__ __attribute__((aligned(16))) char smem[C::kWaves][C::kWaveBytes];
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = lane_id();
+  const int64_t job = (int64_t)blockIdx.x * C::kWaves + w;
+  const int hkv = a.kv.num_kv_heads;
+  if (job >= (int64_t)a.num_tokens * hkv) return;
+  const int tok = (int)(job / hkv);
+  const int g = (int)(job - (int64_t)tok * hkv);
+  const int b = gather_seq_of(a.cu_q, a.num_seqs, tok);
+  const int lk = a.lens_k[b];
+  const int32_t* bt_row = a.kv.bt + (int64_t)b * a.kv.bt_stride;
+  const int32_t* idx_row = a.idx + (int64_t)tok * a.idx_stride;
+  const int pmask = a.kv.page_size - 1;
+
+  lds_t* tiles = (lds_t*)smem[w];                          // [stage][K, V][tile]
+  lds_t* table = (lds_t*)(smem[w] + 4 * C::kTileBytes);   // int32 [kTable]
+  const unsigned tiles_addr = (unsigned)(uintptr_t)tiles;
+  // Per-wave uniform bases (this kv head) and the lane's fixed chunk offset.
+  const uint64_t kbase = (uint64_t)(uintptr_t)(a.kv.k + g * a.kv.k_sh);
+  const uint64_t vbase = (uint64_t)(uintptr_t)(a.kv.v + g * a.kv.v_sh);
+  const unsigned kst = (unsigned)a.kv.k_st, vst = (unsigned)a.kv.v_st;
+  const unsigned chunk_off = (unsigned)(lane % G::kChunks) * 16u;
+  const int row_in_dma = lane / G::kChunks;
+
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  for (int c0 = 0; c0 < a.num_selected; c0 += C::kTable) {
+    const int cnt = min(C::kTable, a.num_selected - c0);
+    const int ntiles = (cnt + C::kTileKeys - 1) / C::kTileKeys;
+    // Translate: every index of the lane, then every block-table entry.
+    constexpr int kPer = C::kTable / 64;
+    int jv[kPer], pv[kPer];
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int e = lane + 64 * k;
+      jv[k] = e < cnt ? __builtin_nontemporal_load(idx_row + c0 + e) : -1;
+    }
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int j = jv[k];
+      pv[k] = (j >= 0 && j < lk) ? bt_row[j >> a.kv.page_shift] : -1;
+    }
+    uint64_t any = 0;
+    int first_valid = 0;
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int j = jv[k], page = pv[k];
+      const bool ok = j >= 0 && j < lk && page >= 0 && page < a.kv.num_pages;
+      pv[k] = ok ? page * a.kv.page_size + (j & pmask) : -1;
+      const uint64_t m = __builtin_amdgcn_ballot_w64(ok);
+      if (any == 0 && m != 0) first_valid = __builtin_amdgcn_readlane(pv[k], __builtin_ctzll(m));
+      any |= m;
+    }
+    if (any == 0) continue;  // nothing selected in this chunk (wave-uniform)
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int e = lane + 64 * k;
+      const int ph = pv[k] >= 0 ? pv[k] : (int)(0x80000000u | (unsigned)first_valid);
+      if (e < ntiles * C::kTileKeys) lds_store<int>(table + 4 * e, ph);
+    }
+    // Copies of tile `it` (K and V) into stage `st`; returns nothing, the
+    // entries' validity is read again when the tile is summed.
+    auto issue = [&](int it, int st) {
+      int ph[C::kDma];
+#pragma unroll
+      for (int u = 0; u < C::kDma; ++u)
+        ph[u] = lds_load<int>(table + 4 * (it * C::kTileKeys + u * C::kRowsPerDma + row_in_dma));
+#pragma unroll
+      for (int u = 0; u < C::kDma; ++u) {
+        const unsigned row = (unsigned)ph[u] & 0x7FFFFFFFu;
+        const unsigned dst = tiles_addr + (2 * st) * C::kTileBytes + u * 1024;
+        dma16_off(kbase, row * kst + chunk_off, dst);
+      }
+#pragma unroll
+      for (int u = 0; u < C::kDma; ++u) {
+        const unsigned row = (unsigned)ph[u] & 0x7FFFFFFFu;
+        const unsigned dst = tiles_addr + (2 * st + 1) * C::kTileBytes + u * 1024;
+        dma16_off(vbase, row * vst + chunk_off, dst);
+      }
+    };
+    // Sum this lane's chunk of its rows of tile `it` (stage `st`): every DMA
+    // lane wrote its 16 bytes at 16 * lane of its 1 KB block, so each lane
+    // reads back exactly what it copied.
+    auto sum = [&](int it, int st) {
+#pragma unroll
+      for (int u = 0; u < C::kDma; ++u) {
+        const int ph = lds_load<int>(table + 4 * (it * C::kTileKeys + u * C::kRowsPerDma + row_in_dma));
+        const u32x4 kx = lds_load<u32x4>(tiles + (2 * st) * C::kTileBytes + u * 1024 + 16 * lane);
+        const u32x4 vx = lds_load<u32x4>(tiles + (2 * st + 1) * C::kTileBytes + u * 1024 + 16 * lane);
+        if (ph >= 0) acc += kx + vx;
+      }
+    };
+    constexpr int D = 2 * C::kDma;  // copies per tile (K and V)
+    issue(0, 0);
+    for (int it = 0; it < ntiles; ++it) {
+      if (it + 1 < ntiles) {
+        issue(it + 1, (it + 1) & 1);
+        wait_vmcnt<D>();  // tile it has landed, tile it + 1 in flight
+      } else {
+        wait_vmcnt<0>();
+      }
+      sum(it, it & 1);
+      // The stage's LDS reads are complete before a later copy refills it.
+      __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4));  // lgkmcnt(0)
+      asm volatile("" ::: "memory");
+    }
+  }
+  // Lanes with the same chunk hold the same words of different rows.
+#pragma unroll
+  for (int off = G::kChunks; off < 64; off <<= 1) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] += (unsigned)__shfl_xor((int)acc[i], off);
+  }
+  if (lane < G::kChunks) {
+    uint32_t* o = a.out + job * (G::kRowBytes / 4) + 4 * lane;
+    *reinterpret_cast<u32x4*>(o) = acc;
+  }
+}
+
+hipError_t launch_gather_sum(const GatherArgs& a, int kv_dtype, hipStream_t s) {
+  constexpr int W = 4;
+  static_assert(GatherCfg<kFP8>::kWaves == W && GatherCfg<kBF16>::kWaves == W, "launch shape");
+  const int64_t jobs = (int64_t)a.num_tokens * a.kv.num_kv_heads;
+  const dim3 grid((unsigned)((jobs + W - 1) / W));
+  if (kv_dtype == kFP8)
+    hipLaunchKernelGGL(gather_sum_kernel<kFP8>, grid, dim3(W * 64), 0, s, a);
+  else
+    hipLaunchKernelGGL(gather_sum_kernel<kBF16>, grid, dim3(W * 64), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace pga

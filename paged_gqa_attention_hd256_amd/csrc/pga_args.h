@@ -93,6 +93,18 @@ struct SparseArgs {
   float* ws_lse;           // [T * hq * splits] natural-log lse of the pieces
 };
 
+// Same-index gather of a selected-token call's K and V rows (gather.hip).
+struct GatherArgs {
+  int32_t num_tokens, num_seqs;
+  const int32_t* cu_q;
+  const int32_t* lens_k;
+  const int32_t* idx;      // [T, idx_stride]
+  int64_t idx_stride;
+  int32_t num_selected;
+  KvArgs kv;               // evenly spaced pool; row byte offsets below 2^32
+  uint32_t* out;           // [T, hkv, row bytes / 4] word sums
+};
+
 // FP8 quantisation of a prefill's inputs (quantize.hip).
 constexpr int kQuantMaxPartials = 1024;  // partial maxima of the reduction pass
 struct QuantArgs {
@@ -143,6 +155,7 @@ hipError_t launch_verify_merge(const VerifyArgs& a, int kv_dtype, int num_wg, hi
 int prefill_tile_tokens(int q_dtype, int kv_dtype, int r);
 hipError_t launch_prefill(const PrefillArgs& a, int q_dtype, int kv_dtype, int q_tiles, hipStream_t s);
 hipError_t launch_sparse(const SparseArgs& a, int kv_dtype, hipStream_t s);
+hipError_t launch_gather_sum(const GatherArgs& a, int kv_dtype, hipStream_t s);
 // Workgroups of the reduction pass for q_chunks 16-byte chunks (1 .. kQuantMaxPartials).
 int quant_amax_blocks(int64_t q_chunks);
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t s);

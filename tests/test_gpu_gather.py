@@ -1,0 +1,66 @@
+"""GPU check of the same-index gather that prices the selected-token call
+(sparse_gather_sum): its per-(row, kv head) sums of the selected K and V
+rows' 32-bit words must equal numpy's exactly (integer sums mod 2^32, so the
+order of the additions does not matter).  Padding, out-of-range entries and
+lists longer than one 1,024-entry chunk are covered; non-selected pool slots
+are NaN-poisoned, which changes the sums if any of them is read."""
+import numpy as np
+import pytest
+
+import workloads as w
+
+pytestmark = pytest.mark.gpu
+
+
+def _expected(p) -> np.ndarray:
+    """Word sums of every row's valid entries, per kv head (numpy, uint64 then mod 2^32)."""
+    words_dtype = np.uint32
+    k = np.ascontiguousarray(p.k_cache).view(words_dtype)
+    v = np.ascontiguousarray(p.v_cache).view(words_dtype)
+    seq = p.token_seq()
+    T, hkv = p.num_tokens, p.num_kv_heads
+    nw = k.shape[-1]
+    out = np.zeros((T, hkv, nw), dtype=np.uint64)
+    for t in range(T):
+        b = seq[t]
+        lk = p.seq_lens_k[b]
+        sel = p.indices[t]
+        sel = sel[(sel >= 0) & (sel < lk)]
+        pages = p.block_table[b, sel // p.page_size]
+        slots = sel % p.page_size
+        if p.kv_layout == "NHD":
+            rows = k[pages, slots].astype(np.uint64) + v[pages, slots].astype(np.uint64)  # [n, hkv, nw]
+        else:
+            rows = (k[pages, :, slots].astype(np.uint64) + v[pages, :, slots].astype(np.uint64))
+        out[t] = rows.sum(0)
+    return (out % (1 << 32)).astype(np.uint32)
+
+
+CASES = [
+    ("fp8_24to2", dict(seed=[101], lq=[20], lk=[3000], hq=24, hkv=2, n=700, kv=w.FP8, pad=0.0)),
+    ("bf16_24to2_pad", dict(seed=[102], lq=[17], lk=[2500], hq=24, hkv=2, n=300, kv=w.BF16, pad=0.3)),
+    ("fp8_long_lists", dict(seed=[103], lq=[5, 3], lk=[6000, 2200], hq=12, hkv=1, n=2100, kv=w.FP8, pad=0.1)),
+    ("bf16_page64", dict(seed=[104], lq=[6], lk=[4000], hq=8, hkv=1, n=1030, kv=w.BF16, pad=0.0, page=64)),
+]
+
+
+@pytest.mark.parametrize("name,c", CASES, ids=[n for n, _ in CASES])
+def test_gather_sum_exact(name, c):
+    import torch
+
+    import paged_gqa_attention_hd256_amd as pga
+    from paged_gqa_attention_hd256_amd import problem_io
+
+    p = w.make_sparse(name, c["seed"], c["lq"], c["lk"], c["hq"], c["hkv"], c["n"], kv_dtype=c["kv"],
+                      page_size=c.get("page", 16), pad_fraction=c["pad"])
+    p.indices[0, 1] = int(p.seq_lens_k[0]) + 5   # an entry past the context: skipped like padding
+    p = w.poison_unused(p)
+    print(f"case {name}", flush=True)
+    dp = problem_io.to_device(p)
+    got = pga.sparse_gather_sum(dp.cu_seqlens_q, dp.seq_lens_k, dp.indices, dp.kv)
+    torch.cuda.synchronize()
+    got = got.cpu().numpy().view(np.uint32)
+    exp = _expected(p)
+    assert got.shape == exp.shape
+    bad = np.argwhere(got != exp)
+    assert bad.size == 0, f"{name}: {len(bad)} sums differ, first at {bad[:3].tolist()}"
