@@ -282,7 +282,7 @@ __global__ __launch_bounds__(256) void verify_merge_kernel(VerifyArgs a) {
     const int incl = wave_incl_scan(cnt);
     const int excl = incl - cnt;
     const int nseg = min(64, sw.segs - s0);
-    const int np = __shfl(incl, nseg - 1);  // pieces of these segments
+    const int np = __builtin_amdgcn_readfirstlane(__shfl(incl, nseg - 1));  // pieces of these segments
     // This lane's 4 head dimensions of the row in piece slot sl, as stored
     // (fp16 for FP8 V, fp32 for BF16 V), and widened to fp32.
     using Raw = std::conditional_t<KV == kFP8, uint2, f32x4>;
@@ -302,10 +302,17 @@ __global__ __launch_bounds__(256) void verify_merge_kernel(VerifyArgs a) {
       }
     };
     for (int c = 0; c < np; c += 64) {
+      // Piece j's segment and that segment's first piece and slot, taken with
+      // scalar reads of lane k's values: a lane shuffle here would sit under
+      // the j < np condition, and a shuffle reads 0 from a lane that is off.
       const int j = c + lane;
-      int sj = 0;
-      for (int k = 1; k < nseg; ++k) sj = j >= __builtin_amdgcn_readlane(excl, k) ? k : sj;
-      const int slot = j < np ? su + s0 + sj + __shfl(first, sj) + (j - __shfl(excl, sj)) : -1;
+      int sj = 0, fj = __builtin_amdgcn_readlane(first, 0), ej = 0;
+      for (int k = 1; k < nseg; ++k) {
+        const int ek = __builtin_amdgcn_readlane(excl, k);
+        const int fk = __builtin_amdgcn_readlane(first, k);
+        if (j >= ek) { sj = k; fj = fk; ej = ek; }
+      }
+      const int slot = j < np ? su + s0 + sj + fj + (j - ej) : -1;
       const float ls = slot >= 0 ? a.ws_lse[(int64_t)slot * a.rows_cap + rho] : kNegInf;
       // The rows of up to 16 pieces are requested with their lse values (one
       // round trip for the usual piece counts); no load past the last piece.
