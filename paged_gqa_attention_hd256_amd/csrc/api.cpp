@@ -116,7 +116,11 @@ int plan_verify(int32_t hq, int32_t hkv, int32_t num_seqs, int32_t max_q_len, in
   if (units * (tiles_bound + int64_t(pga::kVerifySegStartCost) * p.max_segs) > INT32_MAX / 2 ||
       units * p.max_segs + kMaxVerifyWgs > INT32_MAX / 2 || 2 * units + 4 > INT32_MAX / 2)
     return PGA_ERR_UNSUPPORTED;
-  p.wg_cap = static_cast<int32_t>(std::min<int64_t>(kMaxVerifyWgs, std::max<int64_t>(1, cdiv(units * tiles_bound, kMinTilesPerWg))));
+  // Enough workgroups for runs of kMinTilesPerWg positions over the whole
+  // list, start positions included (the kernel's run length is the list
+  // length over the grid, at least kMinTilesPerWg).
+  const int64_t list_bound = units * (tiles_bound + int64_t(pga::kVerifySegStartCost) * p.max_segs);
+  p.wg_cap = static_cast<int32_t>(std::min<int64_t>(kMaxVerifyWgs, std::max<int64_t>(1, cdiv(list_bound, kMinTilesPerWg))));
   if (units > 0 && tiles_bound > 0) {
     const size_t slots = size_t(units) * p.max_segs + p.wg_cap;
     p.ws_o_bytes = slots * p.rows_cap * kHeadDim * sizeof(float);

@@ -31,8 +31,11 @@ struct KvArgs {
 // kVerifySegStartCost empty positions (the cost of starting a piece: query
 // reload, pipeline refill, partial write); a workgroup takes a run of at
 // least kVerifyMinTilesPerWg positions.  Positions and slot indices are int32.
-constexpr int kVerifySegStartCost = 3;
-constexpr int kVerifyMinTilesPerWg = 4;
+// Both values are measured: a start costs about five tiles' time on this part,
+// and with runs of one position the grid reaches 1,024 workgroups also on
+// small batches, where longer minimum runs left most of the chip idle.
+constexpr int kVerifySegStartCost = 5;
+constexpr int kVerifyMinTilesPerWg = 1;
 constexpr int kVerifyMaxWgs = 1024;  // cap of the persistent grid
 
 // Speculative verify: persistent stream-K grid over the key tiles of every

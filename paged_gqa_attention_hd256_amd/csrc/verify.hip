@@ -254,15 +254,18 @@ __global__ __launch_bounds__(256) void verify_merge_kernel(VerifyArgs a) {
   const int b = u / hkv, g = u - (u / hkv) * hkv;
   const int rho = blockIdx.y * 4 + (threadIdx.x >> 6);
   const int lane = lane_id();
+  // Where the unit lies in the flattened order, as verify_kernel recorded it:
+  // loaded together with the sequence's lengths so the two latencies overlap
+  // (the addresses are in bounds for every unit; the values are used only
+  // when the unit has work).
+  const int tu = scalar_load(a.ws_plan + 2 * u);
+  const int su = scalar_load(a.ws_plan + 2 * u + 1);
+  const int tpw = scalar_load(a.ws_plan + 2 * a.num_seqs * hkv);
   const SeqWork sw = seq_work(a, b);
   if (sw.tiles == 0) return;
   const int tok0 = scalar_load(a.cu_q + b);
   const int lq = min(scalar_load(a.cu_q + b + 1) - tok0, a.max_q_len);
   if (rho >= min(a.r * lq, a.rows_cap)) return;
-  // Where the unit lies in the flattened order, as verify_kernel recorded it.
-  const int tu = scalar_load(a.ws_plan + 2 * u);
-  const int su = scalar_load(a.ws_plan + 2 * u + 1);
-  const int tpw = scalar_load(a.ws_plan + 2 * a.num_seqs * hkv);
   const int S = kSegStartCost + a.seg_tiles;
   if (sw.segs == 1 && (tu + kSegStartCost) / tpw == (tu + kSegStartCost + sw.tiles - 1) / tpw)
     return;  // written directly

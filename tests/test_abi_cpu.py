@@ -152,7 +152,9 @@ def _ws_expect(hq, hkv, nseq, maxq, maxk, split):
     seg_tiles = split // 64 if split else max(1, tiles)
     segs = max(1, -(-tiles // seg_tiles))
     units = nseq * hkv
-    wg_cap = min(1024, max(1, -(-units * tiles // 4)))
+    # runs of at least 1 position over the list of tiles plus 5 start
+    # positions per segment, capped at 1024 workgroups
+    wg_cap = min(1024, max(1, units * (tiles + 5 * segs)))
     slots = units * segs + wg_cap
     rows = hq // hkv * maxq
     o = slots * rows * 256 * 4
