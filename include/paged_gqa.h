@@ -314,9 +314,17 @@ int sparse_gather_sum(int32_t num_q_tokens, int32_t num_seqs, const int32_t* cu_
  *                 or on a page id outside [0, num_pages) is not written.
  *   workspace     with the dynamic descale: a device buffer of at least
  *                 prefill_quantize_fp8_workspace_bytes() bytes, 256-byte
- *                 aligned (per-workgroup maxima); otherwise unused
- * Two launches with the dynamic descale (a max-magnitude reduction over Q,
- * then the coding pass), one with a given descale.  Returns PGA_OK or a
+ *                 aligned, any contents (per-workgroup maxima, tagged with a
+ *                 value unique to the call); otherwise unused.  Calls that may
+ *                 run at the same time need workspaces of their own.
+ * With the dynamic descale, a 16-byte aligned q_fp8 and Q of at most
+ * 16 x 1024 x (CU count) 16-byte chunks (64 MiB on 256 CUs): one launch of one
+ * workgroup per CU, each holding its share of Q in registers across a grid
+ * barrier, so Q is read once.  The grid must be resident at once: on a stream
+ * that may use fewer CUs the barrier's bounded wait expires (after more than
+ * 0.2 s) and the codes of the workgroups that waited come out NaN.  Otherwise
+ * two launches (a max-magnitude reduction over Q, then the coding pass, which
+ * reads Q again).  With a given descale: one launch.  Returns PGA_OK or a
  * PGA_ERR_* code.
  */
 int prefill_quantize_fp8(const void* q, int32_t num_q_heads, int32_t num_q_tokens, const float* q_descale_in,

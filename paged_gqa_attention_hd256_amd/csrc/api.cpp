@@ -6,9 +6,12 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
+#include <chrono>
 #include <climits>
 #include <cmath>
 #include <cstdint>
+#include <random>
 
 #include "pga_args.h"
 
@@ -145,6 +148,25 @@ int device_cus() {
 }
 
 int launch_status(hipError_t e) { return e == hipSuccess ? PGA_OK : PGA_ERR_LAUNCH; }
+
+// A 48-bit odd tag unique to each quantisation call of this process: a
+// random start drawn once plus twice the call count (the barrier of the
+// single-read path recognises this call's slots by it, whatever the
+// workspace held before).
+uint64_t next_quant_tag() {
+  static const uint64_t start = [] {
+    uint64_t r = static_cast<uint64_t>(std::chrono::steady_clock::now().time_since_epoch().count());
+    r ^= reinterpret_cast<uintptr_t>(&r) << 16;
+    try {
+      std::random_device rd;
+      r ^= (uint64_t(rd()) << 32) ^ rd();
+    } catch (...) {
+    }
+    return r;
+  }();
+  static std::atomic<uint64_t> calls{0};
+  return ((start + 2 * calls.fetch_add(1, std::memory_order_relaxed)) | 1u) & ((uint64_t(1) << 48) - 1);
+}
 
 }  // namespace
 
@@ -479,7 +501,7 @@ int32_t sparse_paged_attn_splits(int32_t num_q_heads, int32_t num_kv_heads, int3
   return plan_sparse(num_q_heads, num_kv_heads, num_q_tokens, num_selected, p) ? p.splits : 0;
 }
 
-size_t prefill_quantize_fp8_workspace_bytes(void) { return pga::kQuantMaxPartials * sizeof(uint32_t); }
+size_t prefill_quantize_fp8_workspace_bytes(void) { return pga::kQuantWorkspaceBytes; }
 
 int prefill_quantize_fp8(const void* q, int32_t num_q_heads, int32_t num_q_tokens, const float* q_descale_in,
                          void* q_fp8, float* q_descale_out, const void* k_new, const void* v_new, int32_t num_seqs,
@@ -524,6 +546,8 @@ int prefill_quantize_fp8(const void* q, int32_t num_q_heads, int32_t num_q_token
     a.kv = make_kv(kv);
   }
   a.max_blocks = int64_t(device_cus()) * 8;
+  a.num_cus = device_cus();
+  a.tag = next_quant_tag();
   return launch_status(pga::launch_quantize(a, static_cast<hipStream_t>(stream)));
 }
 

@@ -110,6 +110,11 @@ struct GatherArgs {
 
 // FP8 quantisation of a prefill's inputs (quantize.hip).
 constexpr int kQuantMaxPartials = 1024;  // partial maxima of the reduction pass
+constexpr int kQuantResidentChunks = 16;  // Q chunks per thread held by the resident path (64 VGPRs)
+// Workspace: the two-launch path's partial maxima (4 KB), then the resident
+// path's grid barrier: one 128-byte line per workgroup for its tagged
+// partial, then the expired-wait flag word.
+constexpr size_t kQuantWorkspaceBytes = kQuantMaxPartials * sizeof(uint32_t) + 128 * kQuantMaxPartials + 256;
 struct QuantArgs {
   const uint16_t* q;       // [T, hq, 256] bf16
   int64_t q_chunks;        // 16-byte chunks of q: T * hq * 32
@@ -126,6 +131,8 @@ struct QuantArgs {
   const int32_t* cu_k;
   KvArgs kv;               // the FP8 pool the new keys and values are written into
   int64_t max_blocks;      // grid cap of the coding pass
+  int32_t num_cus;         // CUs of the device (the resident path's grid follows from it), 0 = that path off
+  uint64_t tag;            // the resident path's barrier tag, unique to the call (48 bits, odd)
 };
 
 // Device check of the data-dependent preconditions (validate.hip).

@@ -243,7 +243,7 @@ def test_sparse_split_plan(lib):
 
 def quantize(lib, kv=None, **kw):
     a = dict(q=P(), hq=8, ntok=16, qds=None, qfp8=P(20000), qds_out=P(40000), k_new=P(24576), v_new=P(28672),
-             nseq=1, cuq=P(16384), cuk=P(16384 + 64), ws=P(1 << 15), wsb=4096)
+             nseq=1, cuq=P(16384), cuk=P(16384 + 64), ws=P(1 << 15), wsb=4096 + 128 * 1024 + 256)
     a.update(kw)
     kv = kv or kv_struct()
     return lib.prefill_quantize_fp8(a["q"], a["hq"], a["ntok"], a["qds"], a["qfp8"], a["qds_out"], a["k_new"],
@@ -252,7 +252,8 @@ def quantize(lib, kv=None, **kw):
 
 
 def test_quantize_rejects_invalid_arguments(lib):
-    assert lib.prefill_quantize_fp8_workspace_bytes() == 4096
+    # 1024 per-workgroup maxima, then 1024 barrier slots of 128 bytes and a flag block
+    assert lib.prefill_quantize_fp8_workspace_bytes() == 4096 + 128 * 1024 + 256
     assert quantize(lib, q=None) == ENULL
     assert quantize(lib, qfp8=None) == ENULL
     assert quantize(lib, qds_out=None) == ENULL                # the dynamic descale needs somewhere to go
@@ -265,7 +266,7 @@ def test_quantize_rejects_invalid_arguments(lib):
     assert quantize(lib, kv=kv_struct(dtype=1)) == EDTYPE     # the pool must be FP8
     assert quantize(lib, q=P(8)) == EUNSUP                    # q not 16-byte aligned
     assert quantize(lib, k_new=P(24584)) == EUNSUP
-    assert quantize(lib, wsb=4095) == EWS
+    assert quantize(lib, wsb=4096 + 128 * 1024 + 255) == EWS
     assert quantize(lib, ws=None) == EWS
     assert quantize(lib, ws=P((1 << 15) + 16)) == EUNSUP      # workspace not 256-byte aligned
 

@@ -71,7 +71,8 @@ def test_every_finite_bf16_pattern_with_the_dynamic_descale():
     _assert_codes_equal(got, ref, "dynamic, all finite patterns")
 
 
-@pytest.mark.parametrize("T,hq,sigma", [(1, 8, 1.0), (37, 8, 3.0), (300, 16, 1e-3), (4097, 8, 1.0)])
+@pytest.mark.parametrize("T,hq,sigma", [(1, 8, 1.0), (37, 8, 3.0), (300, 16, 1e-3), (4096, 8, 1.0), (4097, 8, 1.0),
+                                        (8193, 8, 0.5)])
 def test_dynamic_descale_on_normal_draws(T, hq, sigma):
     rng = np.random.default_rng(T)
     x = (rng.standard_normal(T * hq * 256) * sigma).astype(np.float32)
@@ -81,6 +82,104 @@ def test_dynamic_descale_on_normal_draws(T, hq, sigma):
     ref, ref_ds = oracle.quantize_fp8(bits)
     assert np.float32(used) == np.float32(ref_ds)
     _assert_codes_equal(got, ref, f"T={T} hq={hq}")
+
+
+def _resident_capacity_chunks() -> int:
+    """16-byte Q chunks the single-read path holds: 16 per thread, 1,024
+    threads per workgroup, one workgroup per CU."""
+    import torch
+    return torch.cuda.get_device_properties(0).multi_processor_count * 1024 * 16
+
+
+def test_dynamic_descale_beyond_the_resident_capacity():
+    """One token more than the registers hold: the two-launch path (Q read
+    twice) must give the same codes and descale."""
+    hq = 8
+    T = _resident_capacity_chunks() // (hq * 32) + 1
+    rng = np.random.default_rng(5)
+    bits = (rng.standard_normal(T * hq * 256, dtype=np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    bits = bits.reshape(T, hq, 256)
+    bits[T - 1, hq - 1, 255] = 0x4300  # the largest magnitude (128.0) in the very last chunk
+    got, used = _quantize_q(bits)
+    ref, ref_ds = oracle.quantize_fp8(bits)
+    assert np.float32(used) == np.float32(ref_ds) == np.float32(128.0 / 448.0)
+    _assert_codes_equal(got, ref, f"T={T} (two-launch path)")
+
+
+def test_resident_path_barrier_slots_from_a_dirty_workspace():
+    """The single-read path on a workspace full of stale bytes: every
+    workgroup (one per CU) publishes its partial maximum under one tag per
+    call, a new tag on the next call, the largest partial is the input's
+    largest magnitude, and no wait expires (the flag word keeps its stale
+    bytes)."""
+    import torch
+    import paged_gqa_attention_hd256_amd as pga
+
+    T, hq = 4097, 8
+    rng = np.random.default_rng(9)
+    bits = (rng.standard_normal(T * hq * 256, dtype=np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    bits = bits.reshape(T, hq, 256)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    ws = torch.full((pga.quantize_workspace_bytes(),), 0xAB, dtype=torch.uint8, device="cuda")
+    ref, ref_ds = oracle.quantize_fp8(bits)
+    tags = []
+    for _ in range(2):
+        codes, used = pga.prefill_quantize_fp8(_bits_to_dev(bits), workspace=ws)
+        torch.cuda.synchronize()
+        words = ws[4096:].view(torch.int64).cpu().numpy().view(np.uint64)
+        slots = words[:1024 * 16:16]
+        assert (slots[cus:] == np.uint64(0xABABABABABABABAB)).all(), "slots beyond the grid written"
+        tag = slots[:cus] >> np.uint64(16)
+        assert (tag == tag[0]).all() and int(tag[0]) & 1 == 1
+        assert int((slots[:cus] & np.uint64(0xFFFF)).max()) == int((bits & 0x7FFF).max())
+        assert words[1024 * 16] == np.uint64(0xABABABABABABABAB), "a barrier wait expired"
+        tags.append(int(tag[0]))
+        assert np.float32(float(used.cpu()[0])) == np.float32(ref_ds)
+        _assert_codes_equal(codes.view(torch.uint8).cpu().numpy(), ref, "dirty workspace")
+    assert tags[0] != tags[1]
+
+
+def test_dynamic_descale_into_an_8_byte_aligned_output():
+    """Codes written to an output that is 8- but not 16-byte aligned (the
+    single-read path stores 16 bytes per lane, so the two-launch path runs)."""
+    import torch
+    import paged_gqa_attention_hd256_amd as pga
+
+    T, hq = 300, 8
+    rng = np.random.default_rng(3)
+    bits = (rng.standard_normal(T * hq * 256, dtype=np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    bits = bits.reshape(T, hq, 256)
+    n = T * hq * 256
+    buf = torch.full((n + 16,), 0x5A, dtype=torch.uint8, device="cuda")
+    out = buf[8:8 + n].view(torch.float8_e4m3fn).view(T, hq, 256)
+    assert out.data_ptr() % 16 == 8
+    _, used = pga.prefill_quantize_fp8(_bits_to_dev(bits), q_fp8=out)
+    torch.cuda.synchronize()
+    ref, ref_ds = oracle.quantize_fp8(bits)
+    assert np.float32(float(used.cpu()[0])) == np.float32(ref_ds)
+    host = buf.cpu().numpy()
+    _assert_codes_equal(host[8:8 + n], ref, "8-byte aligned output")
+    assert (host[:8] == 0x5A).all() and (host[8 + n:] == 0x5A).all(), "bytes outside the output changed"
+
+
+@pytest.mark.parametrize("amax", [2.0 ** -126, 1e-30, 3.0e-5, 0.37, 1.0, 448.0, 1.0e10, 3.0e38])
+def test_dynamic_descale_every_pattern_up_to_amax(amax):
+    """Every finite bf16 pattern of magnitude up to amax (amax itself
+    included, NaNs sprinkled in) under the dynamic descale amax / 448: the
+    quotients reach 448 (1 + 2^-23) at x = amax, and the descales span both
+    division paths (2^-126 / 448 and 3e38 / 448 lie outside the reciprocal's
+    range)."""
+    cap = int(np.array([amax], dtype=np.float32).view(np.uint32)[0] >> 16)
+    mags = np.arange(cap + 1, dtype=np.uint32)
+    bits = np.concatenate([mags, mags | 0x8000]).astype(np.uint16)
+    bits[::997] = 0x7FC1  # NaNs, left out of amax
+    bits[1] = np.uint16(cap)
+    pad = (-bits.size) % (8 * 256)
+    bits = np.concatenate([bits, np.zeros(pad, dtype=np.uint16)]).reshape(-1, 8, 256)
+    got, used = _quantize_q(bits)
+    ref, ref_ds = oracle.quantize_fp8(bits)
+    assert np.float32(used) == np.float32(ref_ds)
+    _assert_codes_equal(got, ref, f"amax {amax}")
 
 
 def test_empty_query_gives_descale_one():
