@@ -486,6 +486,12 @@ int sparse_gather_sum(int32_t num_q_tokens, int32_t num_seqs, const int32_t* cu_
   a.num_selected = num_selected;
   a.kv = make_kv(kv);
   a.out = out;
+  // The list pieces sparse_paged_attn takes for this many rows (up to 16 query
+  // heads per kv head: one row block per kv head, as the workloads have).
+  SparsePlan plan;
+  if (!plan_sparse(16 * a.kv.num_kv_heads, a.kv.num_kv_heads, num_q_tokens, num_selected, plan)) return PGA_ERR_SHAPE;
+  a.splits = plan.splits;
+  a.split_len = plan.split_len;
   return launch_status(pga::launch_gather_sum(a, kv->dtype, static_cast<hipStream_t>(stream)));
 }
 

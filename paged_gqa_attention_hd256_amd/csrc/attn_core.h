@@ -171,9 +171,9 @@ constexpr float kRescaleLog2 = 8.0f;
 // O^T += V^T * P^T over one tile, in two steps: fetch() requests every V
 // fragment of the tile from LDS, multiply() runs the products, so a caller can
 // place other work (the next tile's scores and softmax) between the requests
-// and the products.  Two tile shapes: 16 BF16 keys (one 16-key step, P as a
-// bf16 high and low part) and 32 FP8 keys (one 32-key step, fp16 P, V widened
-// exactly to fp16).
+// and the products.  Three tile shapes: 16 BF16 keys (one 16-key step, P as a
+// bf16 high and low part), 32 FP8 keys (one 32-key step, fp16 P, V widened
+// exactly to fp16) and 16 FP8 keys (one 16-key step, the same precisions).
 template <int KV, int NMB>
 struct TilePV;
 
@@ -229,6 +229,29 @@ struct TilePV<kFP8, 2> {
                       (_Float16)p[1][0], (_Float16)p[1][1], (_Float16)p[1][2], (_Float16)p[1][3]};
 #pragma unroll
     for (int mb = 0; mb < 16; ++mb) st.o[mb] = mfma_f16(fp8x8_to_f16(raw[mb]), pb, st.o[mb]);
+  }
+};
+
+template <>
+struct TilePV<kFP8, 1> {
+  int32_t raw[16];
+  // The 32-key transpose read of TilePV<kFP8, 2>, whose bytes 0..3 in lane l
+  // are V at keys 4 (l / 16) + j, column l % 16 of the d-block: exactly the
+  // 16x16x16 operand.  Its sources for keys 16..31 point at keys 0..15 here
+  // (in bounds); those bytes (4..7) are not used.
+  __device__ __forceinline__ void fetch(const lds_t* vt) {
+    using G = TileGeom<kFP8>;
+    const int lane = lane_id();
+    const int gq = lane >> 4, sl = lane & 15;
+    const int e = sl >> 1, q = sl & 1;
+    const int key = 4 * gq + (e & 3);
+#pragma unroll
+    for (int mb = 0; mb < 16; ++mb) raw[mb] = lds_tr8(vt + G::off(key, mb) + 8 * q)[0];
+  }
+  __device__ __forceinline__ void multiply(WaveState& st, const f32x4 (&p)[1]) const {
+    const f16x4 pb = {(_Float16)p[0][0], (_Float16)p[0][1], (_Float16)p[0][2], (_Float16)p[0][3]};
+#pragma unroll
+    for (int mb = 0; mb < 16; ++mb) st.o[mb] = mfma_f16_k16(fp8x4_to_f16((unsigned)raw[mb]), pb, st.o[mb]);
   }
 };
 

@@ -10,8 +10,10 @@
 // tiles, and does nothing with them but sum their 32-bit words, so its rate is
 // what the gather alone reaches on this part.
 //
-// Work unit: one wave per (query row, kv head) -- the rows that every 16-head
-// block of that kv group reads once each in the attention kernel.  Waves are
+// Work unit: one wave per (query row, kv head, piece of the row's list) -- the
+// rows that every 16-head block of that kv group reads once each in the
+// attention kernel, in the pieces that kernel splits a short batch's lists
+// into (the pieces' sums are added atomically into a zeroed output).  Waves are
 // independent (no barriers).  Per chunk of up to 1,024 list entries the wave
 // translates the entries into a table of physical rows in LDS (negative for an
 // entry that selects nothing, carrying the chunk's first valid row so its copy
@@ -29,13 +31,15 @@ namespace pga {
 
 typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
 
+// The sparse kernel's shape: waves per CU, rows per stage, table entries.
 template <int KV>
 struct GatherCfg {
   using G = TileGeom<KV>;
-  static constexpr int kWaves = 4;
-  static constexpr int kTileKeys = (KV == kFP8) ? 32 : 16;                   // rows of one stage (as the sparse kernel)
-  static constexpr int kTileBytes = G::template tile_bytes<kTileKeys>();     // 8 KB
-  static constexpr int kTable = 1024;                                        // list entries translated at a time
+  static constexpr int kWaves = (KV == kFP8) ? 8 : 4;
+  static constexpr int kWavesPerSimd = kWaves / 4;
+  static constexpr int kTileKeys = 16;                                       // rows of one stage
+  static constexpr int kTileBytes = G::template tile_bytes<kTileKeys>();     // 4 KB (FP8) / 8 KB (BF16)
+  static constexpr int kTable = (KV == kFP8) ? 512 : 1024;                   // list entries translated at a time
   static constexpr int kWaveBytes = 4 * kTileBytes + 4 * kTable;              // 2 stages x (K, V) + table
   static constexpr int kRowsPerDma = 1024 / G::kRowBytes;                    // 4 (FP8) or 2 (BF16)
   static constexpr int kDma = kTileKeys / kRowsPerDma;                       // copies per operand and tile: 8
@@ -52,7 +56,8 @@ __device__ __forceinline__ int gather_seq_of(const int32_t* cu_q, int num_seqs, 
 }
 
 template <int KV>
-__global__ __launch_bounds__(GatherCfg<KV>::kWaves * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(GatherCfg<KV>::kWaves * 64)
+__attribute__((amdgpu_waves_per_eu(GatherCfg<KV>::kWavesPerSimd, GatherCfg<KV>::kWavesPerSimd)))
 void gather_sum_kernel(GatherArgs a) {
   using C = GatherCfg<KV>;
   using G = typename C::G;
@@ -61,9 +66,12 @@ void gather_sum_kernel(GatherArgs a) {
   const int lane = lane_id();
   const int64_t job = (int64_t)blockIdx.x * C::kWaves + w;
   const int hkv = a.kv.num_kv_heads;
-  if (job >= (int64_t)a.num_tokens * hkv) return;
-  const int tok = (int)(job / hkv);
-  const int g = (int)(job - (int64_t)tok * hkv);
+  const int S = a.splits;
+  if (job >= (int64_t)a.num_tokens * hkv * S) return;
+  const int64_t rowjob = job / S;
+  const int sp = (int)(job - rowjob * S);
+  const int tok = (int)(rowjob / hkv);
+  const int g = (int)(rowjob - (int64_t)tok * hkv);
   const int b = gather_seq_of(a.cu_q, a.num_seqs, tok);
   const int lk = a.lens_k[b];
   const int32_t* bt_row = a.kv.bt + (int64_t)b * a.kv.bt_stride;
@@ -81,8 +89,9 @@ void gather_sum_kernel(GatherArgs a) {
   const int row_in_dma = lane / G::kChunks;
 
   u32x4 acc = {0u, 0u, 0u, 0u};
-  for (int c0 = 0; c0 < a.num_selected; c0 += C::kTable) {
-    const int cnt = min(C::kTable, a.num_selected - c0);
+  const int e_end = min((sp + 1) * a.split_len, a.num_selected);
+  for (int c0 = sp * a.split_len; c0 < e_end; c0 += C::kTable) {
+    const int cnt = min(C::kTable, e_end - c0);
     const int ntiles = (cnt + C::kTileKeys - 1) / C::kTileKeys;
     // Translate: every index of the lane, then every block-table entry.
     constexpr int kPer = C::kTable / 64;
@@ -169,15 +178,29 @@ void gather_sum_kernel(GatherArgs a) {
     for (int i = 0; i < 4; ++i) acc[i] += (unsigned)__shfl_xor((int)acc[i], off);
   }
   if (lane < G::kChunks) {
-    uint32_t* o = a.out + job * (G::kRowBytes / 4) + 4 * lane;
-    *reinterpret_cast<u32x4*>(o) = acc;
+    uint32_t* o = a.out + rowjob * (G::kRowBytes / 4) + 4 * lane;
+    if (S == 1) {
+      *reinterpret_cast<u32x4*>(o) = acc;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) atomicAdd(o + i, acc[i]);
+    }
   }
 }
 
+__global__ __launch_bounds__(256) void gather_zero_kernel(uint32_t* out, int64_t words) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < words) out[i] = 0u;
+}
+
 hipError_t launch_gather_sum(const GatherArgs& a, int kv_dtype, hipStream_t s) {
-  constexpr int W = 4;
-  static_assert(GatherCfg<kFP8>::kWaves == W && GatherCfg<kBF16>::kWaves == W, "launch shape");
-  const int64_t jobs = (int64_t)a.num_tokens * a.kv.num_kv_heads;
+  const int W = kv_dtype == kFP8 ? GatherCfg<kFP8>::kWaves : GatherCfg<kBF16>::kWaves;
+  if (a.splits > 1) {
+    const int64_t words = (int64_t)a.num_tokens * a.kv.num_kv_heads * ((kv_dtype == kFP8 ? 256 : 512) / 4);
+    hipLaunchKernelGGL(gather_zero_kernel, dim3((unsigned)((words + 255) / 256)), dim3(256), 0, s, a.out, words);
+    if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+  }
+  const int64_t jobs = (int64_t)a.num_tokens * a.kv.num_kv_heads * a.splits;
   const dim3 grid((unsigned)((jobs + W - 1) / W));
   if (kv_dtype == kFP8)
     hipLaunchKernelGGL(gather_sum_kernel<kFP8>, grid, dim3(W * 64), 0, s, a);

@@ -106,6 +106,8 @@ struct GatherArgs {
   int32_t num_selected;
   KvArgs kv;               // evenly spaced pool; row byte offsets below 2^32
   uint32_t* out;           // [T, hkv, row bytes / 4] word sums
+  int32_t splits;          // pieces of each row's list (the sparse call's plan); > 1: added atomically
+  int32_t split_len;       // entries per piece
 };
 
 // FP8 quantisation of a prefill's inputs (quantize.hip).

@@ -152,6 +152,13 @@ __device__ __forceinline__ f16x8 fp8x8_to_f16(i32x2 w) {
   return f16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
+// Four FP8 E4M3FN codes (one dword) -> four f16 values (exact).
+__device__ __forceinline__ f16x4 fp8x4_to_f16(unsigned w) {
+  f16x2 a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false);
+  f16x2 b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true);
+  return f16x4{a[0], a[1], b[0], b[1]};
+}
+
 __device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
@@ -162,6 +169,10 @@ __device__ __forceinline__ f32x4 mfma_bf16_k16(i16x4 a, i16x4 b, f32x4 c) {
 }
 __device__ __forceinline__ f32x4 mfma_f16(f16x8 a, f16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+// 16x16x16 f16, the lane layout of mfma_bf16_k16.
+__device__ __forceinline__ f32x4 mfma_f16_k16(f16x4 a, f16x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
 }
 
 // Reductions over the four 16-lane groups of a wave (lanes n, n+16, n+32, n+48).

@@ -11,7 +11,7 @@
 // translates a chunk of the row's index list into physical token rows of the
 // pool (index -> block-table page -> page * page_size + slot; negative for an
 // entry that selects nothing) and keeps that table in LDS; then it streams
-// 32-key (FP8) or 16-key (BF16) tiles of K and V through two LDS stages each
+// 16-key tiles of K and V through two LDS stages each
 // by 16-byte DMA whose per-lane source comes from the table, software
 // pipelined: the scores and softmax of tile i + 1 run between the requests
 // and the products of tile i's PV.  Because the table is read from LDS, no
@@ -21,18 +21,21 @@
 
 namespace pga {
 
-constexpr int kSparseTableEntries = 1024;  // index-list chunk held in LDS per wave
-
 template <int KV>
 struct SparseCfg {
   using G = TileGeom<KV>;
-  // Four independent waves per CU: 32-key tiles of FP8 K and V, 16-key tiles
-  // of BF16 (two stages of K and V plus the index table fit 4 x 36 KB of LDS).
-  static constexpr int kWaves = 4;
-  static constexpr int kTileKeys = (KV == kFP8) ? 32 : 16;
+  // Independent waves, 16-key tiles of K and V in two stages each plus the
+  // index table per wave: FP8 runs two waves per SIMD (8 x 18 KB of LDS: a
+  // 512-entry table), BF16 one (4 x 36 KB: a 1,024-entry table).  Measured
+  // on the same-index gather: two waves per SIMD gather FP8 rows about 30 %
+  // faster than one, and BF16 rows (twice the bytes per tile) slower.
+  static constexpr int kWaves = (KV == kFP8) ? 8 : 4;
+  static constexpr int kWavesPerSimd = kWaves / 4;
+  static constexpr int kTileKeys = 16;
   static constexpr int kBlocks = kTileKeys / 16;  // 16-key MFMA blocks per tile
+  static constexpr int kTable = (KV == kFP8) ? 512 : 1024;                       // index-list chunk per wave
   static constexpr int kTileBytes = G::template tile_bytes<kTileKeys>();         // K or V of one tile
-  static constexpr int kWaveBytes = 4 * kTileBytes + 4 * kSparseTableEntries;    // 2 buffers x (K, V) + table
+  static constexpr int kWaveBytes = 4 * kTileBytes + 4 * kTable;                 // 2 buffers x (K, V) + table
   static constexpr int kRowsPerDma = 1024 / G::kRowBytes;
   static constexpr int kDmaPerTile = kTileKeys / kRowsPerDma;                     // per K (or V)
 };
@@ -94,10 +97,11 @@ __device__ __forceinline__ float softmax_deferred(float& m, float& l, f32x4 (&s)
 // 32 x 32 -> 64-bit multiply-add of its physical row index onto a per-lane
 // base, instead of splitting the index into page and slot and forming two
 // 64-bit products (address arithmetic is most of this kernel's vector work).
-// One wave per SIMD (the LDS holds four waves' buffers per CU), so the
-// compiler may spend registers on keeping more loads in flight.
+// Waves per SIMD as SparseCfg sets them (two for FP8, one for BF16: the LDS
+// holds that many waves' buffers), which also bounds their registers.
 template <int KV, bool DENSE>
-__global__ __launch_bounds__(SparseCfg<KV>::kWaves * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(SparseCfg<KV>::kWaves * 64)
+__attribute__((amdgpu_waves_per_eu(SparseCfg<KV>::kWavesPerSimd, SparseCfg<KV>::kWavesPerSimd)))
 void sparse_kernel(SparseArgs a) {
   using C = SparseCfg<KV>;
   using G = typename C::G;
@@ -121,7 +125,7 @@ void sparse_kernel(SparseArgs a) {
 
   char* wbase = smem[w];
   lds_t* tiles = (lds_t*)wbase;                                         // [buf][K, V][tile]
-  lds_t* table = (lds_t*)(wbase + 4 * C::kTileBytes);                   // int32 [kSparseTableEntries]
+  lds_t* table = (lds_t*)(wbase + 4 * C::kTileBytes);                   // int32 [C::kTable]
 
   const int hh = 16 * rb + n;
   const bool row_ok = hh < a.r;
@@ -151,13 +155,13 @@ void sparse_kernel(SparseArgs a) {
   }
 
   const int e_end = min((sp + 1) * a.split_len, a.num_selected);
-  for (int c0 = sp * a.split_len; c0 < e_end; c0 += kSparseTableEntries) {
-    const int cnt = min(kSparseTableEntries, e_end - c0);
+  for (int c0 = sp * a.split_len; c0 < e_end; c0 += C::kTable) {
+    const int cnt = min(C::kTable, e_end - c0);
     const int ntiles = (cnt + C::kTileKeys - 1) / C::kTileKeys;
     // Translate this chunk's entries (and pad the last tile) into physical
     // rows: every index of the lane first, then every block-table entry they
     // need, so the chunk costs two memory round trips rather than two per entry.
-    constexpr int kPer = kSparseTableEntries / 64;  // entries per lane
+    constexpr int kPer = C::kTable / 64;  // entries per lane
     const int nent = ntiles * C::kTileKeys;
     int jv[kPer], pgv[kPer];
 #pragma unroll
@@ -364,8 +368,7 @@ __global__ __launch_bounds__(256) void sparse_merge_kernel(SparseArgs a) {
 hipError_t launch_sparse(const SparseArgs& a, int kv_dtype, hipStream_t s) {
   const int nrb = (a.r + 15) / 16;
   const int64_t jobs = (int64_t)a.num_tokens * a.kv.num_kv_heads * nrb * a.splits;
-  constexpr int W = 4;  // waves per workgroup, both encodings
-  static_assert(SparseCfg<kFP8>::kWaves == W && SparseCfg<kBF16>::kWaves == W, "launch shape");
+  const int W = kv_dtype == kFP8 ? SparseCfg<kFP8>::kWaves : SparseCfg<kBF16>::kWaves;  // waves per workgroup
   const dim3 grid((unsigned)((jobs + W - 1) / W));
   const KvArgs& kv = a.kv;
   const bool dense = kv.k_sp == (int64_t)kv.page_size * kv.k_st && kv.v_sp == (int64_t)kv.page_size * kv.v_st &&

@@ -1,9 +1,11 @@
 """GPU check of the same-index gather that prices the selected-token call
 (sparse_gather_sum): its per-(row, kv head) sums of the selected K and V
 rows' 32-bit words must equal numpy's exactly (integer sums mod 2^32, so the
-order of the additions does not matter).  Padding, out-of-range entries and
-lists longer than one 1,024-entry chunk are covered; non-selected pool slots
-are NaN-poisoned, which changes the sums if any of them is read."""
+order of the additions does not matter).  Padding, out-of-range entries,
+lists longer than one table chunk (512 FP8 / 1,024 BF16 entries), short
+batches (whose lists are split into pieces added atomically) and large ones
+(one wave per whole list) are covered; non-selected pool slots are
+NaN-poisoned, which changes the sums if any of them is read."""
 import numpy as np
 import pytest
 
@@ -41,6 +43,9 @@ CASES = [
     ("bf16_24to2_pad", dict(seed=[102], lq=[17], lk=[2500], hq=24, hkv=2, n=300, kv=w.BF16, pad=0.3)),
     ("fp8_long_lists", dict(seed=[103], lq=[5, 3], lk=[6000, 2200], hq=12, hkv=1, n=2100, kv=w.FP8, pad=0.1)),
     ("bf16_page64", dict(seed=[104], lq=[6], lk=[4000], hq=8, hkv=1, n=1030, kv=w.BF16, pad=0.0, page=64)),
+    # more than 4,096 (row, kv head) jobs: no list pieces
+    ("fp8_unsplit", dict(seed=[105], lq=[2100], lk=[3000], hq=24, hkv=2, n=300, kv=w.FP8, pad=0.1)),
+    ("bf16_unsplit", dict(seed=[106], lq=[2050], lk=[2600], hq=24, hkv=2, n=530, kv=w.BF16, pad=0.0)),
 ]
 
 
