@@ -275,8 +275,10 @@ size_t sparse_paged_attn_workspace_bytes(int32_t num_q_heads, int32_t num_kv_hea
  * results: the row counts and selections whose kernel times it reports).
  * Arguments as in sparse_paged_attn; out is uint32 [num_q_tokens,
  * num_kv_heads, 64 (FP8) or 128 (BF16)], 16-byte aligned.  The pool must be
- * evenly spaced (stride_page = page_size * stride_token for K and V) with
- * every row's byte offset below 2^32; otherwise PGA_ERR_UNSUPPORTED.
+ * evenly spaced (stride_page = page_size * stride_token for K and V), hold at
+ * most 2^24 token rows with token strides below 2^24 bytes, and have every
+ * row's byte offset from its head's base below 2^32; otherwise
+ * PGA_ERR_UNSUPPORTED.
  */
 int sparse_gather_sum(int32_t num_q_tokens, int32_t num_seqs, const int32_t* cu_seqlens_q, const int32_t* seq_lens_k,
                       const int32_t* indices, int64_t index_stride, int32_t num_selected, const pga_paged_kv* kv,

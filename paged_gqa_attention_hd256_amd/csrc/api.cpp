@@ -467,13 +467,17 @@ int sparse_gather_sum(int32_t num_q_tokens, int32_t num_seqs, const int32_t* cu_
   if (num_seqs < 0 || num_q_tokens < 0 || num_selected < 0 || index_stride < num_selected) return PGA_ERR_SHAPE;
   if (num_q_tokens > 0 && num_seqs == 0) return PGA_ERR_SHAPE;
   if (int e = check_kv(kv, kv->num_kv_heads > 0 ? kv->num_kv_heads : 1, -1)) return e;
-  // Evenly spaced token rows, addressed by 32-bit byte offsets from each head's base.
+  // Evenly spaced token rows, addressed by 32-bit byte offsets from each
+  // head's base formed by 24-bit multiplies: at most 2^24 rows, token strides
+  // below 2^24 bytes, every row within 4 GiB of its head's base.
   if (kv->k_stride_page != int64_t(kv->page_size) * kv->k_stride_token ||
       kv->v_stride_page != int64_t(kv->page_size) * kv->v_stride_token)
     return PGA_ERR_UNSUPPORTED;
   const int64_t rows = int64_t(kv->num_pages) * kv->page_size;
   const int64_t st = std::max(kv->k_stride_token, kv->v_stride_token) * elt_bytes(kv->dtype);
-  if (rows > INT32_MAX || rows * st + kHeadDim * elt_bytes(kv->dtype) > int64_t(UINT32_MAX)) return PGA_ERR_UNSUPPORTED;
+  if (std::min(kv->k_stride_token, kv->v_stride_token) <= 0 || st >= (int64_t(1) << 24) ||
+      rows > (int64_t(1) << 24) || (rows - 1) * st + kHeadDim * elt_bytes(kv->dtype) > (int64_t(1) << 32))
+    return PGA_ERR_UNSUPPORTED;
   if (!aligned(out, 16) || (num_selected > 0 && !aligned(indices, 4))) return PGA_ERR_UNSUPPORTED;
   if (num_q_tokens == 0) return PGA_OK;
   pga::GatherArgs a{};

@@ -25,6 +25,8 @@
 // Output: out[row][kv head][w] = sum over the row's valid entries j of the
 // 32-bit words w of K_j and of V_j of that head (row bytes / 4 words), mod
 // 2^32 -- an exact, order-independent checksum.
+#include <type_traits>
+
 #include "causal_stream.h"
 
 namespace pga {
@@ -124,30 +126,32 @@ void gather_sum_kernel(GatherArgs a) {
       const int ph = pv[k] >= 0 ? pv[k] : (int)(0x80000000u | (unsigned)first_valid);
       if (e < ntiles * C::kTileKeys) lds_store<int>(table + 4 * e, ph);
     }
-    // Copies of tile `it` (K and V) into stage `st`; returns nothing, the
-    // entries' validity is read again when the tile is summed.
-    auto issue = [&](int it, int st) {
+    // Copies of tile `it` (K and V) into stage ST (a compile-time constant);
+    // the entries' validity is read again when the tile is summed.  A row's
+    // source offset is one 24-bit multiply-add of the table entry (bits
+    // 24..31, the mask flag among them, are ignored by the multiply).
+    auto issue = [&](int it, auto st_c) {
+      constexpr int st = decltype(st_c)::value;
       int ph[C::kDma];
 #pragma unroll
       for (int u = 0; u < C::kDma; ++u)
         ph[u] = lds_load<int>(table + 4 * (it * C::kTileKeys + u * C::kRowsPerDma + row_in_dma));
 #pragma unroll
       for (int u = 0; u < C::kDma; ++u) {
-        const unsigned row = (unsigned)ph[u] & 0x7FFFFFFFu;
         const unsigned dst = tiles_addr + (2 * st) * C::kTileBytes + u * 1024;
-        dma16_off(kbase, row * kst + chunk_off, dst);
+        dma16_off(kbase, __umul24((unsigned)ph[u], kst) + chunk_off, dst);
       }
 #pragma unroll
       for (int u = 0; u < C::kDma; ++u) {
-        const unsigned row = (unsigned)ph[u] & 0x7FFFFFFFu;
         const unsigned dst = tiles_addr + (2 * st + 1) * C::kTileBytes + u * 1024;
-        dma16_off(vbase, row * vst + chunk_off, dst);
+        dma16_off(vbase, __umul24((unsigned)ph[u], vst) + chunk_off, dst);
       }
     };
-    // Sum this lane's chunk of its rows of tile `it` (stage `st`): every DMA
+    // Sum this lane's chunk of its rows of tile `it` (stage ST): every DMA
     // lane wrote its 16 bytes at 16 * lane of its 1 KB block, so each lane
     // reads back exactly what it copied.
-    auto sum = [&](int it, int st) {
+    auto sum = [&](int it, auto st_c) {
+      constexpr int st = decltype(st_c)::value;
 #pragma unroll
       for (int u = 0; u < C::kDma; ++u) {
         const int ph = lds_load<int>(table + 4 * (it * C::kTileKeys + u * C::kRowsPerDma + row_in_dma));
@@ -157,18 +161,27 @@ void gather_sum_kernel(GatherArgs a) {
       }
     };
     constexpr int D = 2 * C::kDma;  // copies per tile (K and V)
-    issue(0, 0);
-    for (int it = 0; it < ntiles; ++it) {
+    using Even = std::integral_constant<int, 0>;
+    using Odd = std::integral_constant<int, 1>;
+    // One tile; PAR = it & 1 (the loop is unrolled by two so the stage is a
+    // compile-time constant).
+    auto step = [&](int it, auto par_c) {
+      constexpr int par = decltype(par_c)::value;
       if (it + 1 < ntiles) {
-        issue(it + 1, (it + 1) & 1);
+        issue(it + 1, std::integral_constant<int, par ^ 1>{});
         wait_vmcnt<D>();  // tile it has landed, tile it + 1 in flight
       } else {
         wait_vmcnt<0>();
       }
-      sum(it, it & 1);
+      sum(it, par_c);
       // The stage's LDS reads are complete before a later copy refills it.
       __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4));  // lgkmcnt(0)
       asm volatile("" ::: "memory");
+    };
+    issue(0, Even{});
+    for (int it = 0; it < ntiles; it += 2) {
+      step(it, Even{});
+      if (it + 1 < ntiles) step(it + 1, Odd{});
     }
   }
   // Lanes with the same chunk hold the same words of different rows.

@@ -17,6 +17,9 @@
 // and the products of tile i's PV.  Because the table is read from LDS, no
 // vector-memory load sits between the DMA instructions and their counter can
 // be waited on exactly.
+#include <algorithm>
+#include <type_traits>
+
 #include "causal_stream.h"
 
 namespace pga {
@@ -92,13 +95,17 @@ __device__ __forceinline__ float softmax_deferred(float& m, float& l, f32x4 (&s)
 }
 
 // DENSE: the pool's token rows are evenly spaced (page stride = page_size x
-// token stride, for K and for V; the "NHD" layout), the token strides fit 32
-// bits and every physical row index fits 31 bits.  Then a row's address is one
-// 32 x 32 -> 64-bit multiply-add of its physical row index onto a per-lane
-// base, instead of splitting the index into page and slot and forming two
-// 64-bit products (address arithmetic is most of this kernel's vector work).
-// Waves per SIMD as SparseCfg sets them (two for FP8, one for BF16: the LDS
-// holds that many waves' buffers), which also bounds their registers.
+// token stride, for K and for V; the "NHD" layout), there are at most 2^24
+// physical rows, the token strides are below 2^24 bytes and every row of a kv
+// head lies within 4 GiB of that head's base.  Then a copy's source is the
+// head's base (wave-uniform) plus a 32-bit byte offset formed by one 24-bit
+// multiply-add of the table entry (whose bits 24..31, the mask flag among
+// them, the multiply ignores) onto the lane's chunk offset, instead of
+// splitting the index into page and slot and forming 64-bit products (address
+// arithmetic is most of this kernel's vector work).  Other pools take the
+// general form.  Waves per SIMD as SparseCfg sets them (two for FP8, one for
+// BF16: the LDS holds that many waves' buffers), which also bounds their
+// registers.
 template <int KV, bool DENSE>
 __global__ __launch_bounds__(SparseCfg<KV>::kWaves * 64)
 __attribute__((amdgpu_waves_per_eu(SparseCfg<KV>::kWavesPerSimd, SparseCfg<KV>::kWavesPerSimd)))
@@ -142,16 +149,16 @@ void sparse_kernel(SparseArgs a) {
   WaveState st;
   st.init();
   // Per-lane parts of the DMA source addresses that do not change from tile
-  // to tile: the 16-byte chunk this lane copies of its row (swizzled by row).
+  // to tile: the byte offset of the 16-byte chunk this lane copies of its row
+  // (swizzled by the row's place in the tile).
   const uint64_t zaddr = (uint64_t)(uintptr_t)g_zero16;
+  const uint64_t kb = (uint64_t)(uintptr_t)kbase, vb = (uint64_t)(uintptr_t)vbase;
   const uint32_t kst = (uint32_t)a.kv.k_st, vst = (uint32_t)a.kv.v_st;
-  uint64_t kb[C::kDmaPerTile], vb[C::kDmaPerTile];
+  uint32_t co[C::kDmaPerTile];
 #pragma unroll
   for (int u = 0; u < C::kDmaPerTile; ++u) {
     const int row = u * C::kRowsPerDma + lane / G::kChunks;
-    const int chunk = (lane % G::kChunks) ^ (row & (G::kChunks - 1));
-    kb[u] = (uint64_t)(uintptr_t)kbase + chunk * 16;
-    vb[u] = (uint64_t)(uintptr_t)vbase + chunk * 16;
+    co[u] = (uint32_t)((lane % G::kChunks) ^ (row & (G::kChunks - 1))) * 16u;
   }
 
   const int e_end = min((sp + 1) * a.split_len, a.num_selected);
@@ -202,8 +209,10 @@ void sparse_kernel(SparseArgs a) {
       if (e < nent) lds_store<int>(table + 4 * e, ph);
     }
 
-    // Copies of one operand (K or V) of tile it into stage buf.
-    auto issue = [&](int it, int buf, bool is_v) {
+    // Copies of one operand (K or V) of tile it into stage BUF (a compile-time
+    // constant, so the stage's LDS offsets are immediates).
+    auto issue = [&](int it, auto buf_c, bool is_v) {
+      constexpr int buf = decltype(buf_c)::value;
       // Every table read of the tile first, so their LDS latency is paid once
       // (the copies below are ordered memory operations: no load moves past them).
       int physv[C::kDmaPerTile];
@@ -214,25 +223,28 @@ void sparse_kernel(SparseArgs a) {
       for (int u = 0; u < C::kDmaPerTile; ++u) {
         const int row0 = u * C::kRowsPerDma;
         const int phys = physv[u];
-        uint64_t src;
+        lds_t* dst = tiles + (2 * buf + (is_v ? 1 : 0)) * C::kTileBytes + row0 * G::kRowBytes;
         if constexpr (DENSE) {
-          src = (uint64_t)((uint32_t)phys & 0x7FFFFFFFu) * (is_v ? vst : kst) + (is_v ? vb[u] : kb[u]);
+          const uint32_t off = __umul24((uint32_t)phys, is_v ? vst : kst) + co[u];
+          dma16_off(is_v ? vb : kb, off, (unsigned)(uintptr_t)dst);
         } else {
           const int row = row0 + lane / G::kChunks;
           const int chunk = (lane % G::kChunks) ^ (row & (G::kChunks - 1));
           const int64_t page = phys >> a.kv.page_shift;
           const int slot = phys & pmask;
-          src = phys >= 0 ? (uint64_t)(uintptr_t)((is_v ? vbase : kbase) + page * (is_v ? a.kv.v_sp : a.kv.k_sp) +
-                                                  slot * (is_v ? a.kv.v_st : a.kv.k_st) + chunk * 16)
-                          : zaddr;
+          const uint64_t src = phys >= 0 ? (uint64_t)(uintptr_t)((is_v ? vbase : kbase) + page * (is_v ? a.kv.v_sp : a.kv.k_sp) +
+                                                                 slot * (is_v ? a.kv.v_st : a.kv.k_st) + chunk * 16)
+                                         : zaddr;
+          dma16((const void*)(uintptr_t)src, dst);
         }
-        dma16((const void*)(uintptr_t)src, tiles + (2 * buf + (is_v ? 1 : 0)) * C::kTileBytes + row0 * G::kRowBytes);
       }
     };
-    // Scores and softmax of tile it (K in stage it & 1); the accumulators are
-    // left for the caller to rescale after the previous tile's product.
-    auto scores_softmax = [&](int it, f32x4 (&sc)[C::kBlocks], bool& grow) -> float {
-      tile_scores<KV, C::kBlocks, true>(tiles + (2 * (it & 1) + 0) * C::kTileBytes, qf, sc);
+    // Scores and softmax of tile it (K in stage PAR = it & 1); the
+    // accumulators are left for the caller to rescale after the previous
+    // tile's product.
+    auto scores_softmax = [&](int it, auto par_c, f32x4 (&sc)[C::kBlocks], bool& grow) -> float {
+      constexpr int par = decltype(par_c)::value;
+      tile_scores<KV, C::kBlocks, true>(tiles + (2 * par + 0) * C::kTileBytes, qf, sc);
       const lds_t* tt = table + 4 * (it * C::kTileKeys);
       const i32x4 v0 = lds_load<i32x4>(tt + 4 * (4 * gq));
       i32x4 v1 = v0;
@@ -249,33 +261,40 @@ void sparse_kernel(SparseArgs a) {
     // it + 1 and the product of tile it, so neither waits on the other's
     // latencies.  K runs two tiles ahead of the product, V one: K(it + 2) goes
     // into the K stage of tile it (its scores were computed an iteration
-    // earlier), V(it + 1) into the V stage of tile it - 1.
+    // earlier), V(it + 1) into the V stage of tile it - 1.  The loop is
+    // unrolled by two so each stage index is a compile-time constant.
     constexpr int D = C::kDmaPerTile;
-    issue(0, 0, false);
-    issue(0, 0, true);
+    using Even = std::integral_constant<int, 0>;
+    using Odd = std::integral_constant<int, 1>;
+    issue(0, Even{}, false);
+    issue(0, Even{}, true);
     if (ntiles > 1) {
-      issue(1, 1, false);
+      issue(1, Odd{}, false);
       wait_vmcnt<2 * D>();  // K(0)
     } else {
       wait_vmcnt<D>();
     }
     f32x4 p[C::kBlocks];
     bool grow;
-    scores_softmax(0, p, grow);  // the accumulators are still zero
-    for (int it = 0; it + 1 < ntiles; ++it) {
+    scores_softmax(0, Even{}, p, grow);  // the accumulators are still zero
+    // One iteration; PAR = it & 1.
+    auto step = [&](int it, auto par_c) {
+      constexpr int par = decltype(par_c)::value;
+      using Same = std::integral_constant<int, par>;
+      using Other = std::integral_constant<int, par ^ 1>;
       if (it + 2 < ntiles) {
-        issue(it + 2, it & 1, false);
-        issue(it + 1, (it + 1) & 1, true);
+        issue(it + 2, Same{}, false);
+        issue(it + 1, Other{}, true);
         wait_vmcnt<2 * D>();  // K(it + 1) and V(it) have landed
       } else {
-        issue(it + 1, (it + 1) & 1, true);
+        issue(it + 1, Other{}, true);
         wait_vmcnt<D>();
       }
       TilePV<KV, C::kBlocks> pv;
-      pv.fetch(tiles + (2 * (it & 1) + 1) * C::kTileBytes);
+      pv.fetch(tiles + (2 * par + 1) * C::kTileBytes);
       f32x4 pn[C::kBlocks];
       bool gn;
-      const float an = scores_softmax(it + 1, pn, gn);
+      const float an = scores_softmax(it + 1, Other{}, pn, gn);
       pv.multiply(st, p);
       if (gn) {
 #pragma unroll
@@ -283,6 +302,10 @@ void sparse_kernel(SparseArgs a) {
       }
 #pragma unroll
       for (int mb = 0; mb < C::kBlocks; ++mb) p[mb] = pn[mb];
+    };
+    for (int it = 0; it + 1 < ntiles; it += 2) {
+      step(it, Even{});
+      if (it + 2 < ntiles) step(it + 1, Odd{});
     }
     wait_vmcnt<0>();
     TilePV<KV, C::kBlocks> pv;
@@ -371,9 +394,12 @@ hipError_t launch_sparse(const SparseArgs& a, int kv_dtype, hipStream_t s) {
   const int W = kv_dtype == kFP8 ? SparseCfg<kFP8>::kWaves : SparseCfg<kBF16>::kWaves;  // waves per workgroup
   const dim3 grid((unsigned)((jobs + W - 1) / W));
   const KvArgs& kv = a.kv;
+  const int64_t rows = (int64_t)kv.num_pages * kv.page_size;
+  const int64_t row_bytes = kv_dtype == kFP8 ? 256 : 512;
   const bool dense = kv.k_sp == (int64_t)kv.page_size * kv.k_st && kv.v_sp == (int64_t)kv.page_size * kv.v_st &&
-                     kv.k_st > 0 && kv.v_st > 0 && kv.k_st < (int64_t(1) << 32) && kv.v_st < (int64_t(1) << 32) &&
-                     (int64_t)kv.num_pages * kv.page_size < (int64_t(1) << 31);
+                     kv.k_st > 0 && kv.v_st > 0 && kv.k_st < (int64_t(1) << 24) && kv.v_st < (int64_t(1) << 24) &&
+                     rows <= (int64_t(1) << 24) &&
+                     (rows - 1) * std::max(kv.k_st, kv.v_st) + row_bytes <= (int64_t(1) << 32);
   if (kv_dtype == kFP8) {
     if (dense)
       hipLaunchKernelGGL((sparse_kernel<kFP8, true>), grid, dim3(W * 64), 0, s, a);

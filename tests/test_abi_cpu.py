@@ -290,3 +290,22 @@ def test_validate_rejects_invalid_host_arguments(lib):
     assert validate(lib, idx=P(30000), ntok=-1, stride=8, nsel=8) == ESHAPE
     assert validate(lib, idx=P(30000), stride=4, nsel=8) == ESHAPE
     assert validate(lib, counts=P(40002)) == EUNSUP
+
+
+def gather(lib, kv=None, **kw):
+    a = dict(ntok=8, nseq=1, cuq=P(16384), lk=P(16384 + 64), idx=P(30000), stride=64, nsel=64, out=P(20480))
+    a.update(kw)
+    kv = kv or kv_struct()
+    return lib.sparse_gather_sum(a["ntok"], a["nseq"], a["cuq"], a["lk"], a["idx"], a["stride"], a["nsel"],
+                                 ctypes.byref(kv), a["out"], None)
+
+
+def test_gather_rejects_pools_its_offsets_cannot_address(lib):
+    assert gather(lib, ntok=0) == OK
+    assert gather(lib, out=None) == ENULL
+    # Not evenly spaced: the page stride is not page_size token strides.
+    assert gather(lib, kv=kv_struct(k_stride_page=16 * 256 + 256)) == EUNSUP
+    # More than 2^24 token rows, a token stride of 2^24 bytes, rows past 4 GiB.
+    assert gather(lib, kv=kv_struct(num_pages=(1 << 20) + 1)) == EUNSUP
+    assert gather(lib, kv=kv_struct(k_stride_token=1 << 24, k_stride_page=16 << 24)) == EUNSUP
+    assert gather(lib, kv=kv_struct(num_pages=1 << 20, k_stride_token=1 << 13, k_stride_page=16 << 13)) == EUNSUP
