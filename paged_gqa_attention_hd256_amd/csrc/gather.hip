@@ -17,10 +17,11 @@
 // independent (no barriers).  Per chunk of up to 1,024 list entries the wave
 // translates the entries into a table of physical rows in LDS (negative for an
 // entry that selects nothing, carrying the chunk's first valid row so its copy
-// stays in bounds), then streams tiles of K and V rows through two LDS stages,
-// copies of tile i + 1 in flight while tile i is summed.  Only the pool's
-// evenly spaced layout is handled (page stride = page size x token stride for
-// K and for V), the one the benchmarked selections use.
+// stays in bounds), then streams tiles of K and V rows through two LDS stages
+// each on the attention kernel's schedule (K two tiles ahead of V's use, V
+// one).  Only the pool's evenly spaced layout is handled (page stride = page
+// size x token stride for K and for V), the one the benchmarked selections
+// use.
 //
 // Output: out[row][kv head][w] = sum over the row's valid entries j of the
 // 32-bit words w of K_j and of V_j of that head (row bytes / 4 words), mod
@@ -66,14 +67,16 @@ void gather_sum_kernel(GatherArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[C::kWaves][C::kWaveBytes];
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = lane_id();
-  const int64_t job = (int64_t)blockIdx.x * C::kWaves + w;
   const int hkv = a.kv.num_kv_heads;
   const int S = a.splits;
-  if (job >= (int64_t)a.num_tokens * hkv * S) return;
-  const int64_t rowjob = job / S;
-  const int sp = (int)(job - rowjob * S);
-  const int tok = (int)(rowjob / hkv);
-  const int g = (int)(rowjob - (int64_t)tok * hkv);
+  // Jobs of one kv head: (row, piece), pieces fastest; the heads spread over
+  // the XCDs as in the sparse kernel.
+  const HeadJob hj = head_job(blockIdx.x, w, C::kWaves, hkv);
+  if (hj.j >= (int64_t)a.num_tokens * S) return;
+  const int g = hj.g;
+  const int tok = (int)(hj.j / S);
+  const int sp = (int)(hj.j - (int64_t)tok * S);
+  const int64_t rowjob = (int64_t)tok * hkv + g;
   const int b = gather_seq_of(a.cu_q, a.num_seqs, tok);
   const int lk = a.lens_k[b];
   const int32_t* bt_row = a.kv.bt + (int64_t)b * a.kv.bt_stride;
@@ -126,11 +129,11 @@ void gather_sum_kernel(GatherArgs a) {
       const int ph = pv[k] >= 0 ? pv[k] : (int)(0x80000000u | (unsigned)first_valid);
       if (e < ntiles * C::kTileKeys) lds_store<int>(table + 4 * e, ph);
     }
-    // Copies of tile `it` (K and V) into stage ST (a compile-time constant);
-    // the entries' validity is read again when the tile is summed.  A row's
-    // source offset is one 24-bit multiply-add of the table entry (bits
-    // 24..31, the mask flag among them, are ignored by the multiply).
-    auto issue = [&](int it, auto st_c) {
+    // Copies of one operand (K or V) of tile `it` into stage ST (a
+    // compile-time constant).  A row's source offset is one 24-bit
+    // multiply-add of the table entry (bits 24..31, the mask flag among them,
+    // are ignored by the multiply).
+    auto issue = [&](int it, auto st_c, bool is_v) {
       constexpr int st = decltype(st_c)::value;
       int ph[C::kDma];
 #pragma unroll
@@ -138,51 +141,78 @@ void gather_sum_kernel(GatherArgs a) {
         ph[u] = lds_load<int>(table + 4 * (it * C::kTileKeys + u * C::kRowsPerDma + row_in_dma));
 #pragma unroll
       for (int u = 0; u < C::kDma; ++u) {
-        const unsigned dst = tiles_addr + (2 * st) * C::kTileBytes + u * 1024;
-        dma16_off(kbase, __umul24((unsigned)ph[u], kst) + chunk_off, dst);
-      }
-#pragma unroll
-      for (int u = 0; u < C::kDma; ++u) {
-        const unsigned dst = tiles_addr + (2 * st + 1) * C::kTileBytes + u * 1024;
-        dma16_off(vbase, __umul24((unsigned)ph[u], vst) + chunk_off, dst);
+        const unsigned dst = tiles_addr + (2 * st + (is_v ? 1 : 0)) * C::kTileBytes + u * 1024;
+        dma16_off(is_v ? vbase : kbase, __umul24((unsigned)ph[u], is_v ? vst : kst) + chunk_off, dst);
       }
     };
-    // Sum this lane's chunk of its rows of tile `it` (stage ST): every DMA
-    // lane wrote its 16 bytes at 16 * lane of its 1 KB block, so each lane
-    // reads back exactly what it copied.
-    auto sum = [&](int it, auto st_c) {
+    // Add this lane's chunk of its valid rows of one operand of tile `it`
+    // (stage ST): every DMA lane wrote its 16 bytes at 16 * lane of its 1 KB
+    // block, so each lane reads back exactly what it copied.
+    // Every read is issued before any sum, and the mask is applied by an AND,
+    // so no read waits behind a branch on the previous one.
+    auto sum = [&](int it, auto st_c, bool is_v) {
       constexpr int st = decltype(st_c)::value;
+      int ph[C::kDma];
+      u32x4 x[C::kDma];
 #pragma unroll
       for (int u = 0; u < C::kDma; ++u) {
-        const int ph = lds_load<int>(table + 4 * (it * C::kTileKeys + u * C::kRowsPerDma + row_in_dma));
-        const u32x4 kx = lds_load<u32x4>(tiles + (2 * st) * C::kTileBytes + u * 1024 + 16 * lane);
-        const u32x4 vx = lds_load<u32x4>(tiles + (2 * st + 1) * C::kTileBytes + u * 1024 + 16 * lane);
-        if (ph >= 0) acc += kx + vx;
+        ph[u] = lds_load<int>(table + 4 * (it * C::kTileKeys + u * C::kRowsPerDma + row_in_dma));
+        x[u] = lds_load<u32x4>(tiles + (2 * st + (is_v ? 1 : 0)) * C::kTileBytes + u * 1024 + 16 * lane);
+      }
+#pragma unroll
+      for (int u = 0; u < C::kDma; ++u) {
+        const unsigned m = ph[u] >= 0 ? ~0u : 0u;
+        acc += x[u] & u32x4{m, m, m, m};
       }
     };
-    constexpr int D = 2 * C::kDma;  // copies per tile (K and V)
-    using Even = std::integral_constant<int, 0>;
-    using Odd = std::integral_constant<int, 1>;
-    // One tile; PAR = it & 1 (the loop is unrolled by two so the stage is a
-    // compile-time constant).
-    auto step = [&](int it, auto par_c) {
-      constexpr int par = decltype(par_c)::value;
-      if (it + 1 < ntiles) {
-        issue(it + 1, std::integral_constant<int, par ^ 1>{});
-        wait_vmcnt<D>();  // tile it has landed, tile it + 1 in flight
-      } else {
-        wait_vmcnt<0>();
-      }
-      sum(it, par_c);
-      // The stage's LDS reads are complete before a later copy refills it.
+    // The stage's LDS reads are complete before a later copy refills it.
+    auto reads_done = [] {
       __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4));  // lgkmcnt(0)
       asm volatile("" ::: "memory");
     };
-    issue(0, Even{});
-    for (int it = 0; it < ntiles; it += 2) {
-      step(it, Even{});
-      if (it + 1 < ntiles) step(it + 1, Odd{});
+    // The attention kernel's copy schedule: K two tiles ahead of V's use, V
+    // one; iteration it takes K(it + 1) and V(it) (where that kernel computes
+    // the scores of tile it + 1 and the product of tile it).  Unrolled by two
+    // so each stage is a compile-time constant.
+    constexpr int D = C::kDma;  // copies per operand and tile
+    using Even = std::integral_constant<int, 0>;
+    using Odd = std::integral_constant<int, 1>;
+    issue(0, Even{}, false);
+    issue(0, Even{}, true);
+    if (ntiles > 1) {
+      issue(1, Odd{}, false);
+      wait_vmcnt<2 * D>();  // K(0)
+    } else {
+      wait_vmcnt<D>();
     }
+    sum(0, Even{}, false);
+    reads_done();
+    auto step = [&](int it, auto par_c) {
+      constexpr int par = decltype(par_c)::value;
+      using Same = std::integral_constant<int, par>;
+      using Other = std::integral_constant<int, par ^ 1>;
+      if (it + 2 < ntiles) {
+        issue(it + 2, Same{}, false);
+        issue(it + 1, Other{}, true);
+        wait_vmcnt<2 * D>();  // K(it + 1) and V(it) have landed
+      } else {
+        issue(it + 1, Other{}, true);
+        wait_vmcnt<D>();
+      }
+      sum(it, Same{}, true);
+      sum(it + 1, Other{}, false);
+      reads_done();
+    };
+    for (int it = 0; it + 1 < ntiles; it += 2) {
+      step(it, Even{});
+      if (it + 2 < ntiles) step(it + 1, Odd{});
+    }
+    wait_vmcnt<0>();
+    if ((ntiles - 1) & 1)
+      sum(ntiles - 1, Odd{}, true);
+    else
+      sum(ntiles - 1, Even{}, true);
+    reads_done();
   }
   // Lanes with the same chunk hold the same words of different rows.
 #pragma unroll
@@ -213,8 +243,7 @@ hipError_t launch_gather_sum(const GatherArgs& a, int kv_dtype, hipStream_t s) {
     hipLaunchKernelGGL(gather_zero_kernel, dim3((unsigned)((words + 255) / 256)), dim3(256), 0, s, a.out, words);
     if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
   }
-  const int64_t jobs = (int64_t)a.num_tokens * a.kv.num_kv_heads * a.splits;
-  const dim3 grid((unsigned)((jobs + W - 1) / W));
+  const dim3 grid((unsigned)head_job_grid((int64_t)a.num_tokens * a.splits, W, a.kv.num_kv_heads));
   if (kv_dtype == kFP8)
     hipLaunchKernelGGL(gather_sum_kernel<kFP8>, grid, dim3(W * 64), 0, s, a);
   else

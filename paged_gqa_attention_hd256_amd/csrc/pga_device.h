@@ -45,6 +45,38 @@ enum KvKind { kBF16 = 1, kFP8 = 2 };
 __device__ __attribute__((aligned(16))) static const uint32_t g_zero16[4] = {0, 0, 0, 0};
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+// MI355X dispatches workgroup b of a launch to XCD b % 8, and each XCD has an
+// L2 of its own.
+constexpr int kXcds = 8;
+
+// Jobs of independent waves that each belong to one of hkv kv heads: job j of
+// head g is wave j % W of the j / W-th workgroup of that head.  When hkv
+// divides the XCD count, every workgroup of an XCD works on one head (the
+// XCDs take the heads in turn), so an XCD's L2 holds the rows of one head
+// instead of all of them; the launch then needs kXcds * ceil(ceil(L / W) /
+// (kXcds / hkv)) workgroups for L jobs per head.  Otherwise the heads take
+// consecutive jobs in turn (ceil(hkv * L / W) workgroups).
+struct HeadJob {
+  int g;      // kv head
+  int64_t j;  // job index among that head's jobs
+};
+__device__ __forceinline__ HeadJob head_job(int b, int w, int W, int hkv) {
+  if (kXcds % hkv == 0) {
+    const int per = kXcds / hkv, xcd = b % kXcds;
+    return HeadJob{xcd % hkv, ((int64_t)(b / kXcds) * per + xcd / hkv) * W + w};
+  }
+  const int64_t job = (int64_t)b * W + w;
+  return HeadJob{(int)(job % hkv), job / hkv};
+}
+inline int64_t head_job_grid(int64_t jobs_per_head, int W, int hkv) {
+  const int64_t wgs = (jobs_per_head + W - 1) / W;
+  if (kXcds % hkv == 0) {
+    const int per = kXcds / hkv;
+    return kXcds * ((wgs + per - 1) / per);
+  }
+  return (hkv * jobs_per_head + W - 1) / W;
+}
 __device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
 
 // Wait until at most N vector-memory loads of this wave are outstanding (loads

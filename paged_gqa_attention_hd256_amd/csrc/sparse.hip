@@ -119,14 +119,14 @@ void sparse_kernel(SparseArgs a) {
   const int n = lane & 15, gq = lane >> 4;
   const int nrb = (a.r + 15) >> 4;                  // 16-row blocks per kv group
   const int S = a.splits;
-  const int64_t job = (int64_t)blockIdx.x * C::kWaves + w;
-  const int64_t njobs = (int64_t)a.num_tokens * a.kv.num_kv_heads * nrb * S;
-  if (job >= njobs) return;
-  const int64_t rowjob = job / S;
-  const int sp = (int)(job - rowjob * S);  // piece of the row's index list
-  const int tok = (int)(rowjob / (a.kv.num_kv_heads * nrb));
-  const int rem = (int)(rowjob - (int64_t)tok * a.kv.num_kv_heads * nrb);
-  const int g = rem / nrb, rb = rem - (rem / nrb) * nrb;
+  // Jobs of one kv head: (token, row block, piece), pieces fastest.
+  const HeadJob hj = head_job(blockIdx.x, w, C::kWaves, a.kv.num_kv_heads);
+  if (hj.j >= (int64_t)a.num_tokens * nrb * S) return;
+  const int g = hj.g;
+  const int64_t rowjob = hj.j / S;
+  const int sp = (int)(hj.j - rowjob * S);  // piece of the row's index list
+  const int tok = (int)(rowjob / nrb);
+  const int rb = (int)(rowjob - (int64_t)tok * nrb);
   const int b = seq_of(a.cu_q, a.num_seqs, tok);
   const int lk = a.lens_k[b];
 
@@ -390,9 +390,8 @@ __global__ __launch_bounds__(256) void sparse_merge_kernel(SparseArgs a) {
 
 hipError_t launch_sparse(const SparseArgs& a, int kv_dtype, hipStream_t s) {
   const int nrb = (a.r + 15) / 16;
-  const int64_t jobs = (int64_t)a.num_tokens * a.kv.num_kv_heads * nrb * a.splits;
   const int W = kv_dtype == kFP8 ? SparseCfg<kFP8>::kWaves : SparseCfg<kBF16>::kWaves;  // waves per workgroup
-  const dim3 grid((unsigned)((jobs + W - 1) / W));
+  const dim3 grid((unsigned)head_job_grid((int64_t)a.num_tokens * nrb * a.splits, W, a.kv.num_kv_heads));
   const KvArgs& kv = a.kv;
   const int64_t rows = (int64_t)kv.num_pages * kv.page_size;
   const int64_t row_bytes = kv_dtype == kFP8 ? 256 : 512;
