@@ -162,22 +162,31 @@ void sparse_kernel(SparseArgs a) {
   }
 
   const int e_end = min((sp + 1) * a.split_len, a.num_selected);
+  constexpr int kPer = C::kTable / 64;  // entries per lane
+  // The index entries of the chunk at c0 (-1 past the piece).  Each row's
+  // list is read exactly once: non-temporal, so it does not displace the K/V
+  // rows that other rows of the sequence reuse from L2.
+  auto load_indices = [&](int c0, int (&jv)[kPer]) {
+    const int cnt = min(C::kTable, e_end - c0);
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int e = lane + 64 * k;
+      jv[k] = e < cnt ? __builtin_nontemporal_load(idx_row + c0 + e) : -1;
+    }
+  };
+  int jnext[kPer];
+  load_indices(sp * a.split_len, jnext);
   for (int c0 = sp * a.split_len; c0 < e_end; c0 += C::kTable) {
     const int cnt = min(C::kTable, e_end - c0);
     const int ntiles = (cnt + C::kTileKeys - 1) / C::kTileKeys;
     // Translate this chunk's entries (and pad the last tile) into physical
-    // rows: every index of the lane first, then every block-table entry they
-    // need, so the chunk costs two memory round trips rather than two per entry.
-    constexpr int kPer = C::kTable / 64;  // entries per lane
+    // rows: its indices were requested a chunk ahead; every block-table entry
+    // they need is requested at once, so the chunk's translation waits for one
+    // memory round trip rather than two per entry.
     const int nent = ntiles * C::kTileKeys;
     int jv[kPer], pgv[kPer];
 #pragma unroll
-    for (int k = 0; k < kPer; ++k) {
-      const int e = lane + 64 * k;
-      // Each row's list is read exactly once: non-temporal, so it does not
-      // displace the K/V rows that other rows of the sequence reuse from L2.
-      jv[k] = e < cnt ? __builtin_nontemporal_load(idx_row + c0 + e) : -1;
-    }
+    for (int k = 0; k < kPer; ++k) jv[k] = jnext[k];
 #pragma unroll
     for (int k = 0; k < kPer; ++k) {
       const int j = jv[k];
@@ -201,6 +210,9 @@ void sparse_kernel(SparseArgs a) {
       if (anyv == 0 && m != 0) first_valid = __builtin_amdgcn_readlane(physv[k], __builtin_ctzll(m));
       anyv |= m;
     }
+    // The next chunk's indices travel while this chunk's tiles stream: they
+    // are requested before the first copy, and first used after the last.
+    if (c0 + C::kTable < e_end) load_indices(c0 + C::kTable, jnext);
     if (anyv == 0) continue;  // nothing selected in this chunk (wave-uniform)
 #pragma unroll
     for (int k = 0; k < kPer; ++k) {
