@@ -121,7 +121,10 @@ typedef struct pga_paged_kv {
  * fixed: a fixed set of persistent workgroups takes equal shares of the list
  * of (sequence, kv head, 64-key tile) work, so a history is cut where those
  * shares end, and additionally into segments of at most kv_split_tokens keys
- * when that is set.
+ * when that is set.  Small calls (num_seqs * num_kv_heads * ceil(max_kv_len /
+ * 64) <= 256 tiles, at most 64 per history) skip that plan: one workgroup per
+ * 64-key tile, its partial rows merged the same way (kv_split_tokens then
+ * changes nothing, every piece being one tile).
  *
  *   q             [T, num_q_heads, 256] bf16 (q_dtype must be PGA_DTYPE_BF16)
  *   q_descale     device scalar or NULL; used as a factor on the scores
@@ -174,8 +177,9 @@ int paged_attn_verify_merge(const void* q, int32_t q_dtype, const float* q_desca
  * from the first such call until the process ends.  The call allocates and
  * frees nothing.  The scratch holds, for units = num_seqs * num_kv_heads,
  * segs = ceil(ceil(max_kv_len / 64) / (kv_split_tokens / 64)) (1 when
- * kv_split_tokens is 0), slots = units * segs + the persistent grid (at most
- * 2 workgroups per compute unit) and rows = (num_q_heads / num_kv_heads) *
+ * kv_split_tokens is 0), slots = units * segs + the grid (at most 2
+ * workgroups per compute unit; units * ceil(max_kv_len / 64) for the small
+ * calls above) and rows = (num_q_heads / num_kv_heads) *
  * max_q_len: slots * rows * 256 partial values (2 bytes each for FP8 V, 4 for
  * BF16 V) plus slots * rows lse values; a call whose bounds need more returns
  * PGA_ERR_SCRATCH and launches nothing.  Nothing in the scratch needs to

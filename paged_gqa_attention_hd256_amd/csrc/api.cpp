@@ -258,6 +258,12 @@ static int prepare_verify(const void* q, int32_t q_dtype, const float* q_descale
     return e;
   const int occupancy = kv->dtype == kFP8 ? 2 : 1;  // workgroups per CU the LDS allows
   num_wg = std::max(1, std::min(p.wg_cap, device_cus() * occupancy));
+  // Small calls: one workgroup per tile of each unit, no plan (at most as many
+  // slots as the stream-K plan's workspace holds: wg_cap >= units * tiles).
+  const int64_t tiles_bound = cdiv(max_kv_len, kTileKeys);
+  const int64_t static_tiles = int64_t(num_seqs) * kv->num_kv_heads * tiles_bound;
+  const bool plan_free = tiles_bound > 0 && tiles_bound <= 64 && static_tiles <= pga::kVerifyStaticMaxTiles;
+  if (plan_free) num_wg = static_cast<int>(static_tiles);
   size_t ws_o_bytes = p.ws_o_bytes, ws_lse_bytes = p.ws_lse_bytes;
   if (use_scratch) {
     if (p.ws_bytes > 0) {
@@ -298,6 +304,7 @@ static int prepare_verify(const void* q, int32_t q_dtype, const float* q_descale
   a.ws_o = workspace;
   a.ws_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + ws_o_bytes);
   a.ws_plan = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + ws_o_bytes + ws_lse_bytes);
+  a.static_tiles = plan_free ? static_cast<int32_t>(tiles_bound) : 0;
   return PGA_OK;
 }
 
@@ -345,6 +352,7 @@ int paged_attn_verify(const void* q, int32_t q_dtype, const float* q_descale, in
   if (nothing) return PGA_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (int e = launch_status(pga::launch_verify(a, kv->dtype, num_wg, s))) return e;
+  if (a.static_tiles == 1) return PGA_OK;  // every unit fits one tile: all written directly
   return launch_status(pga::launch_verify_merge(a, kv->dtype, num_wg, s));
 }
 
@@ -363,6 +371,7 @@ int paged_attn_verify_noalloc(const void* q, int32_t q_dtype, const float* q_des
   if (nothing) return PGA_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (int e = launch_status(pga::launch_verify(a, kv->dtype, num_wg, s))) return e;
+  if (a.static_tiles == 1) return PGA_OK;  // every unit fits one tile: all written directly
   return launch_status(pga::launch_verify_merge(a, kv->dtype, num_wg, s));
 }
 

@@ -37,6 +37,9 @@ struct KvArgs {
 constexpr int kVerifySegStartCost = 5;
 constexpr int kVerifyMinTilesPerWg = 1;
 constexpr int kVerifyMaxWgs = 1024;  // cap of the persistent grid
+// Calls whose host bounds give at most this many tiles over all units (and
+// at most 64 per unit) run one workgroup per tile without the plan.
+constexpr int kVerifyStaticMaxTiles = 256;
 
 // Speculative verify: persistent stream-K grid over the key tiles of every
 // (sequence, kv head) unit; see verify.hip.
@@ -58,6 +61,8 @@ struct VerifyArgs {
                            // units (v_descale not applied): fp16 for FP8 V (|x| <= 448), fp32 for BF16 V
   float* ws_lse;           // [slots, rows_cap] fp32 natural-log lse of the partials
   int32_t* ws_plan;        // [units][2]: first tile, first segment of each unit; then tiles per workgroup
+  int32_t static_tiles;    // > 0: plan-free mode, workgroup w takes tile w % static_tiles of unit
+                           //   w / static_tiles and writes slot w (0: the stream-K plan)
 };
 
 // Prefill against a cached prefix: one workgroup per (tile of query tokens,

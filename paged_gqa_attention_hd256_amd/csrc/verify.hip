@@ -19,6 +19,14 @@
 // exp(lse - max lse).  This replaces a fixed segment count, which on a batch
 // of uneven lengths leaves a nearly empty second round of workgroups
 // (Modifications: segments chosen from CU parallelism and per-segment work).
+//
+// Small calls (static_tiles > 0: at most kVerifyStaticMaxTiles tiles over all
+// units by the host bounds) skip the plan: workgroup w takes tile w % P of
+// unit w / P (P = static_tiles, the host bound of a unit's tiles) and writes
+// its piece to slot w, or the output when it is the unit's only tile.  Its
+// first reads (the lengths and each wave's block-table entry, taken at the
+// host bound) then go out together, one memory round trip before the copies
+// instead of a plan scan before them.
 #include <type_traits>
 
 #include "causal_stream.h"
@@ -108,6 +116,68 @@ __device__ PlanPos plan_scan(const VerifyArgs& a, int num_wg, int target_t, int 
   return p;
 }
 
+// One piece: keys [k_lo, k_hi) of kv head g of sequence b (tok0 = its first
+// query token, lq / lk its clamped lengths; `first`: the page ids of the
+// range's first two tiles for this wave).  A direct piece writes the bf16
+// output and lse; any other writes its rows divided by their sums (V code
+// units) and their natural-log lse to workspace slot `slot`.
+template <int KV>
+__device__ __forceinline__ void verify_piece(const VerifyArgs& a, CausalSmem<KV, 4>& sm, int b, int g, int tok0,
+                                             int lq, int lk, int k_lo, int k_hi, int2 first, bool direct,
+                                             int64_t slot) {
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = lane_id();
+  const int n = lane & 15, gq = lane >> 4;
+  const float c2 = a.c2_base * load_scale(a.q_ds) * load_scale(a.kv.k_ds);
+  const float vds = load_scale(a.kv.v_ds);
+  const int rows = min(a.r * lq, a.rows_cap);
+  const int rho = 16 * w + n;  // this lane's softmax row
+  const bool row_ok = rho < rows;
+  const int t = row_ok ? rho / a.r : 0;
+  const int head = g * a.r + (row_ok ? rho - t * a.r : 0);
+  const int64_t tok = tok0 + t;
+  const bool live = 16 * w < rows;
+  const int32_t* bt_row = a.kv.bt + (int64_t)b * a.kv.bt_stride;
+  QFragT<KV> qf;
+  load_q<kBF16, KV>(qf, a.q, tok, a.hq, head, row_ok);
+  const int klim = row_ok ? min(lk - lq + t, k_hi - 1) : -1;
+  const int min_lim = min(lk - lq, k_hi - 1);
+  RowStat rs;
+  rs.init();
+  f32x4 o[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  f32x4 lsum = {0.f, 0.f, 0.f, 0.f};
+  stream_keys<true>(sm, a.kv, bt_row, g, k_lo, k_hi, first,
+              SplitTile<kBF16, KV, 4>{qf, c2 * qf.rscale, klim, min_lim, live, rs, o, lsum, sm.x});
+  const float lrow = finish_rows(lsum, live, sm.x);
+  if (row_ok && gq == 0) {
+    const float lse = lrow > 0.f ? (rs.m + log2f(lrow)) * kLn2 : kNegInf;
+    if (!direct)
+      a.ws_lse[slot * a.rows_cap + rho] = lse;
+    else if (a.lse)
+      a.lse[tok * a.hq + head] = lse;
+  }
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb) {
+    const int rr = 16 * rb + n;
+    if (rr < rows) {
+      const float l = sm.x.row[rr];
+      const float inv = l > 0.f ? vds / l : 0.f;
+      if (direct) {
+        const int t2 = rr / a.r;
+        store_share_bf16<4>(o, rb, inv, a.out + ((tok0 + t2) * (int64_t)a.hq + g * a.r + rr - t2 * a.r) * kHeadDim);
+      } else if constexpr (KV == kFP8) {
+        store_share_f16<4>(o, rb, l > 0.f ? 1.f / l : 0.f,
+                          static_cast<uint16_t*>(a.ws_o) + (slot * a.rows_cap + rr) * kHeadDim);
+      } else {
+        store_share_f32<4>(o, rb, l > 0.f ? 1.f / l : 0.f,
+                          static_cast<float*>(a.ws_o) + (slot * a.rows_cap + rr) * kHeadDim);
+      }
+    }
+  }
+}
+
 template <int KV>
 __global__ __launch_bounds__(256, (KV == kFP8) ? 2 : 1) void verify_kernel(VerifyArgs a) {
   __shared__ CausalSmem<KV, 4> sm;
@@ -116,7 +186,31 @@ __global__ __launch_bounds__(256, (KV == kFP8) ? 2 : 1) void verify_kernel(Verif
   const int hkv = a.kv.num_kv_heads;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = lane_id();
-  const int n = lane & 15, gq = lane >> 4;
+
+  if (a.static_tiles > 0) {
+    // Tile k of unit u; the wave's block-table entry is read at the host
+    // bound of the keys (in the row), with the lengths, and kept only if the
+    // wave's first key exists (a wave past the end copies zeros, which its
+    // mask gives probability 0).
+    const int P = a.static_tiles;
+    const int u = wg / P, k = wg - (wg / P) * P;
+    const int b = u / hkv, g = u - (u / hkv) * hkv;
+    const int32_t* bt_row = a.kv.bt + (int64_t)b * a.kv.bt_stride;
+    const int key0 = 64 * k + 16 * w;
+    const int pidx = __builtin_amdgcn_readfirstlane(min(key0, a.max_kv_len - 1) >> a.kv.page_shift);
+    const int tok0 = scalar_load(a.cu_q + b);
+    const int tq1 = scalar_load(a.cu_q + b + 1);
+    const int lk_raw = scalar_load(a.lens_k + b);
+    const int page = scalar_load(bt_row + pidx);
+    const int lq = min(tq1 - tok0, a.max_q_len);
+    const int lk = min(lk_raw, a.max_kv_len);
+    const int tiles = (lq > 0 && lk > 0) ? (lk + 63) >> 6 : 0;
+    if (k >= tiles) return;  // workgroup-uniform
+    const int k_hi = min(64 * k + 64, lk);
+    verify_piece<KV>(a, sm, b, g, tok0, lq, lk, 64 * k, k_hi, int2{key0 < k_hi ? page : -1, 0}, tiles == 1,
+                     (int64_t)wg);
+    return;
+  }
 
   if (w == 0) {
     // This workgroup's run starts at tile wg * tpw; tpw needs the total first.
@@ -144,8 +238,6 @@ __global__ __launch_bounds__(256, (KV == kFP8) ? 2 : 1) void verify_kernel(Verif
   int g = (t0 - tprefix * hkv) / sw.span;
   int tu = tprefix * hkv + g * sw.span;   // start of unit (b, g) in the flattened list
   int su = sprefix * hkv + g * sw.segs;   // first segment of unit (b, g)
-  const float c2 = a.c2_base * load_scale(a.q_ds) * load_scale(a.kv.k_ds);
-  const float vds = load_scale(a.kv.v_ds);
 
   if (wg == 0 && threadIdx.x == 0) a.ws_plan[2 * a.num_seqs * hkv] = tpw;
   int cur = t0;
@@ -172,58 +264,13 @@ __global__ __launch_bounds__(256, (KV == kFP8) ? 2 : 1) void verify_kernel(Verif
     const int tok0 = scalar_load(a.cu_q + b);
     const int lq = min(scalar_load(a.cu_q + b + 1) - tok0, a.max_q_len);
     const int lk = min(scalar_load(a.lens_k + b), a.max_kv_len);
-    const int rows = min(a.r * lq, a.rows_cap);
-    const int rho = 16 * w + n;  // this lane's softmax row
-    const bool row_ok = rho < rows;
-    const int t = row_ok ? rho / a.r : 0;
-    const int head = g * a.r + (row_ok ? rho - t * a.r : 0);
-    const int64_t tok = tok0 + t;
-    const bool live = 16 * w < rows;
     const int k_lo = lt0 * 64, k_hi = min(lt1 * 64, lk);
     const int32_t* bt_row = a.kv.bt + (int64_t)b * a.kv.bt_stride;
-    const int2 first = first_pages<4>(a.kv, bt_row, k_lo, k_hi);
-    QFragT<KV> qf;
-    load_q<kBF16, KV>(qf, a.q, tok, a.hq, head, row_ok);
-    const int klim = row_ok ? min(lk - lq + t, k_hi - 1) : -1;
-    const int min_lim = min(lk - lq, k_hi - 1);
-    RowStat rs;
-    rs.init();
-    f32x4 o[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-    f32x4 lsum = {0.f, 0.f, 0.f, 0.f};
-    stream_keys<true>(sm, a.kv, bt_row, g, k_lo, k_hi, first,
-                SplitTile<kBF16, KV, 4>{qf, c2 * qf.rscale, klim, min_lim, live, rs, o, lsum, sm.x});
-    const float lrow = finish_rows(lsum, live, sm.x);
     // A run that covers a whole uncut unit writes the output; any other piece
-    // writes its normalised fp32 rows and their lse to its workspace slot.
+    // writes its partial rows to its workspace slot.
     const bool direct = lt0 == s * a.seg_tiles && lt1 == lts1 && sw.segs == 1;
-    const int64_t slot = (int64_t)su + s + wg;
-    if (row_ok && gq == 0) {
-      const float lse = lrow > 0.f ? (rs.m + log2f(lrow)) * kLn2 : kNegInf;
-      if (!direct)
-        a.ws_lse[slot * a.rows_cap + rho] = lse;
-      else if (a.lse)
-        a.lse[tok * a.hq + head] = lse;
-    }
-#pragma unroll
-    for (int rb = 0; rb < 4; ++rb) {
-      const int rr = 16 * rb + n;
-      if (rr < rows) {
-        const float l = sm.x.row[rr];
-        const float inv = l > 0.f ? vds / l : 0.f;
-        if (direct) {
-          const int t2 = rr / a.r;
-          store_share_bf16<4>(o, rb, inv, a.out + ((tok0 + t2) * (int64_t)a.hq + g * a.r + rr - t2 * a.r) * kHeadDim);
-        } else if constexpr (KV == kFP8) {
-          store_share_f16<4>(o, rb, l > 0.f ? 1.f / l : 0.f,
-                            static_cast<uint16_t*>(a.ws_o) + (slot * a.rows_cap + rr) * kHeadDim);
-        } else {
-          store_share_f32<4>(o, rb, l > 0.f ? 1.f / l : 0.f,
-                            static_cast<float*>(a.ws_o) + (slot * a.rows_cap + rr) * kHeadDim);
-        }
-      }
-    }
+    verify_piece<KV>(a, sm, b, g, tok0, lq, lk, k_lo, k_hi, first_pages<4>(a.kv, bt_row, k_lo, k_hi), direct,
+                     (int64_t)su + s + wg);
     cur = tu + xe;
     if (xe == sw.span) {  // next unit: next kv head, or the next sequence with work
       tu += sw.span;
@@ -361,6 +408,77 @@ __global__ __launch_bounds__(256) void verify_merge_kernel(VerifyArgs a) {
   if (lane == 0 && a.lse) a.lse[tok * a.hq + head] = wsum > 0.f ? mx + logf(wsum) : kNegInf;
 }
 
+// The merge of the plan-free mode: unit u's pieces are slots u * P + k for
+// its tiles k (P = static_tiles <= 64).  One wave per query row; the lse of
+// every slot of the unit (one per lane) and the rows of the first 16 are read
+// together with the lengths, before it is known how many of them the unit
+// has (the reads stay in the workspace; slots past its tiles hold stale
+// values and get weight 0).
+template <int KV>
+__global__ __launch_bounds__(256) void verify_merge_tiles_kernel(VerifyArgs a) {
+  const int hkv = a.kv.num_kv_heads;
+  const int u = blockIdx.x;
+  const int b = u / hkv, g = u - (u / hkv) * hkv;
+  const int rho = blockIdx.y * 4 + (threadIdx.x >> 6);
+  const int lane = lane_id();
+  if (rho >= a.rows_cap) return;
+  using Raw = std::conditional_t<KV == kFP8, uint2, f32x4>;
+  auto load_part = [&](int64_t sl) -> Raw {
+    const int64_t off = (sl * a.rows_cap + rho) * kHeadDim + 4 * lane;
+    if constexpr (KV == kFP8)
+      return *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(a.ws_o) + off);
+    else
+      return *reinterpret_cast<const f32x4*>(static_cast<const float*>(a.ws_o) + off);
+  };
+  auto widen = [](Raw r) -> f32x4 {
+    if constexpr (KV == kFP8) {
+      const f16x4 h = __builtin_bit_cast(f16x4, r);
+      return f32x4{(float)h[0], (float)h[1], (float)h[2], (float)h[3]};
+    } else {
+      return r;
+    }
+  };
+  const int P = a.static_tiles;
+  const int64_t base = (int64_t)u * P;
+  const float ls_all = lane < P ? a.ws_lse[(base + lane) * a.rows_cap + rho] : kNegInf;
+  Raw v[16];
+#pragma unroll
+  for (int k = 0; k < 16; ++k) v[k] = k < P ? load_part(base + k) : Raw{};
+  const SeqWork sw = seq_work(a, b);
+  const int tok0 = scalar_load(a.cu_q + b);
+  const int lq = min(scalar_load(a.cu_q + b + 1) - tok0, a.max_q_len);
+  if (sw.tiles <= 1 || rho >= min(a.r * lq, a.rows_cap)) return;  // written directly / no such row
+  const float ls = lane < sw.tiles ? ls_all : kNegInf;
+  const float mx = wave_max(ls);
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  float wsum = 0.f;
+  if (mx != kNegInf) {
+    const float wgt = ls == kNegInf ? 0.f : __expf(ls - mx);
+    wsum = wave_sum(wgt);
+    for (int q = 0; q < sw.tiles; q += 16) {
+      if (q > 0) {
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+          v[k] = Raw{};
+          if (q + k < sw.tiles) v[k] = load_part(base + q + k);
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const float wq = q + k < sw.tiles ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wgt), q + k)) : 0.f;
+        if (wq != 0.f) acc += wq * widen(v[k]);
+      }
+    }
+  }
+  const float inv = wsum > 0.f ? load_scale(a.kv.v_ds) / wsum : 0.f;
+  const int t = rho / a.r;
+  const int head = g * a.r + (rho - t * a.r);
+  const int64_t tok = tok0 + t;
+  uint16_t* op = a.out + (tok * a.hq + head) * kHeadDim + 4 * lane;
+  *reinterpret_cast<uint2*>(op) = make_uint2(pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv));
+  if (lane == 0 && a.lse) a.lse[tok * a.hq + head] = wsum > 0.f ? mx + logf(wsum) : kNegInf;
+}
+
 hipError_t launch_verify(const VerifyArgs& a, int kv_dtype, int num_wg, hipStream_t s) {
   if (kv_dtype == kFP8)
     hipLaunchKernelGGL(verify_kernel<kFP8>, dim3(num_wg), dim3(256), 0, s, a);
@@ -371,10 +489,16 @@ hipError_t launch_verify(const VerifyArgs& a, int kv_dtype, int num_wg, hipStrea
 
 hipError_t launch_verify_merge(const VerifyArgs& a, int kv_dtype, int num_wg, hipStream_t s) {
   dim3 grid(a.num_seqs * a.kv.num_kv_heads, (a.rows_cap + 3) / 4);
-  if (kv_dtype == kFP8)
+  if (a.static_tiles > 0) {
+    if (kv_dtype == kFP8)
+      hipLaunchKernelGGL(verify_merge_tiles_kernel<kFP8>, grid, dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL(verify_merge_tiles_kernel<kBF16>, grid, dim3(256), 0, s, a);
+  } else if (kv_dtype == kFP8) {
     hipLaunchKernelGGL(verify_merge_kernel<kFP8>, grid, dim3(256), 0, s, a);
-  else
+  } else {
     hipLaunchKernelGGL(verify_merge_kernel<kBF16>, grid, dim3(256), 0, s, a);
+  }
   return hipGetLastError();
 }
 

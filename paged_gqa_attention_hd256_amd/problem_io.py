@@ -66,11 +66,20 @@ class DeviceProblem:
     quant: Optional[QuantBuffers] = None
 
 
-def to_device(p, device="cuda", kv_split_tokens: Optional[int] = None) -> DeviceProblem:
+def to_device(p, device="cuda", kv_split_tokens: Optional[int] = None,
+              max_kv_len: Optional[int] = None) -> DeviceProblem:
+    """Device copies of problem p.  max_kv_len overrides the host bound of the
+    key lengths (default: their maximum); the block table then gets columns
+    of page 0 up to that bound, which no visible key reads."""
     q = _codes_to_tensor(p.q, p.q_dtype, device)
     k = _codes_to_tensor(p.k_cache, p.kv_dtype, device)
     v = _codes_to_tensor(p.v_cache, p.kv_dtype, device)
-    bt = torch.from_numpy(np.ascontiguousarray(p.block_table, dtype=np.int32)).to(device)
+    bt_np = np.ascontiguousarray(p.block_table, dtype=np.int32)
+    if max_kv_len is not None:
+        cols = -(-int(max_kv_len) // int(p.page_size))
+        if bt_np.shape[1] < cols:
+            bt_np = np.pad(bt_np, ((0, 0), (0, cols - bt_np.shape[1])))
+    bt = torch.from_numpy(np.ascontiguousarray(bt_np)).to(device)
     kv = PagedKV(k, v, bt, layout=p.kv_layout, k_descale=_scalar(p.k_descale, device),
                  v_descale=_scalar(p.v_descale, device))
     cu_q = torch.from_numpy(np.ascontiguousarray(p.cu_seqlens_q, dtype=np.int32)).to(device)
@@ -86,6 +95,9 @@ def to_device(p, device="cuda", kv_split_tokens: Optional[int] = None) -> Device
     lse = torch.empty((T, Hq), dtype=torch.float32, device=device)
     max_q = int(np.diff(p.cu_seqlens_q).max()) if len(p.seq_lens_k) else 0
     max_k = int(np.max(p.seq_lens_k)) if len(p.seq_lens_k) else 0
+    if max_kv_len is not None:
+        assert max_kv_len >= max_k, "max_kv_len below a key length"
+        max_k = int(max_kv_len)
     split = p.kv_split_tokens if kv_split_tokens is None else kv_split_tokens
     ws = None
     if p.mode == "verify":

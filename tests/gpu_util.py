@@ -51,16 +51,17 @@ class Guarded:
             f"{what}: {bad_head} elements written before and {bad_tail} after the buffer"
 
 
-def run_gpu(p, split=None, repeat=1, stage="all", with_lse=True):
+def run_gpu(p, split=None, repeat=1, stage="all", with_lse=True, max_kv_len=None):
     """Run problem p through the library ``repeat`` times and return the output
     bits and lse of each run.  out, lse and the workspace sit inside sentinel
     margins that are checked after every run; with_lse=False passes no lse
-    pointer (the returned lse is then all NaN)."""
+    pointer (the returned lse is then all NaN); max_kv_len overrides the host
+    bound of the key lengths."""
     import numpy as np
     import torch
     from paged_gqa_attention_hd256_amd import problem_io
 
-    dp = problem_io.to_device(p, kv_split_tokens=split)
+    dp = problem_io.to_device(p, kv_split_tokens=split, max_kv_len=max_kv_len)
     g_out = Guarded(dp.out.numel(), torch.bfloat16, OUT_MARGIN, OUT_SENTINEL)
     dp.out = g_out.view.view(dp.out.shape)
     g_lse = None

@@ -25,8 +25,9 @@ def test_benchmarked_kernels_exist():
     defined = _kernel_names()
     for mode, k in bench.KERNELS.items():
         assert k["main"] in defined, f"{mode}: {k['main']} is not a kernel in csrc/"
-        if "merge" in k:
-            assert k["merge"] in defined, f"{mode}: {k['merge']} is not a kernel in csrc/"
+        for key in ("merge", "merge_tiles"):
+            if key in k:
+                assert k[key] in defined, f"{mode}: {k[key]} is not a kernel in csrc/"
         for f in k["sources"]:
             assert os.path.exists(os.path.join(CSRC, f)), f
 

@@ -20,11 +20,26 @@ from tests.gpu_util import assert_parity, bf16_bits_to_f64, run_gpu
 pytestmark = pytest.mark.gpu
 
 
-def _check(p, split=None, what=None):
-    print(f"case {p.name} split={split}", flush=True)
+def _check(p, split=None, what=None, max_kv_len=None):
+    print(f"case {p.name} split={split} max_kv_len={max_kv_len}", flush=True)
     ref, ref_lse = oracle.attention(p)
-    bits, lse = run_gpu(p, split=split)
+    bits, lse = run_gpu(p, split=split, max_kv_len=max_kv_len)
     return assert_parity(bits, lse, ref, ref_lse, what=what or p.name)
+
+
+# Verify runs small calls (at most 256 tiles of 64 keys over all (sequence,
+# kv head) units by the host bounds, at most 64 per unit) without the work
+# plan, one workgroup per tile.  A host bound of the key lengths above 64
+# tiles sends the same problem through the planned (stream-K) path.
+def _planned_bound(p):
+    return max(int(np.max(p.seq_lens_k)), 64 * 65)
+
+
+def _plan_free(p, max_kv_len=None):
+    mk = int(np.max(p.seq_lens_k)) if max_kv_len is None else max_kv_len
+    tiles = -(-mk // 64)
+    units = len(p.seq_lens_k) * p.num_kv_heads
+    return 0 < tiles <= 64 and units * tiles <= 256
 
 
 # ------------------------------------------------------------------ verify ---
@@ -61,15 +76,35 @@ def _verify_problem(name, c, poison=False):
 @pytest.mark.parametrize("name,c", VERIFY_CASES, ids=[n for n, _ in VERIFY_CASES])
 @pytest.mark.parametrize("split", [0, 64, 256, 1 << 20])
 def test_verify_parity(name, c, split):
+    # The planned path: the host bound of the key lengths is raised past 64
+    # tiles, so every case runs through the stream-K plan with this split.
     p = _verify_problem(name, c, poison=True)
-    _check(p, split=split, what=f"{name}/split{split}")
+    mk = _planned_bound(p)
+    assert not _plan_free(p, mk)
+    _check(p, split=split, what=f"{name}/split{split}/planned", max_kv_len=mk)
+
+
+@pytest.mark.parametrize("name,c", VERIFY_CASES, ids=[n for n, _ in VERIFY_CASES])
+def test_verify_parity_at_exact_bound(name, c):
+    # The host bound equal to the longest history: the small cases run
+    # without the plan (one workgroup per tile), the long ones with it.
+    p = _verify_problem(name, c, poison=True)
+    _check(p, split=0, what=f"{name}/{'plan-free' if _plan_free(p) else 'planned'}")
+
+
+def test_verify_plan_free_covers_most_small_cases():
+    free = [n for n, c in VERIFY_CASES if _plan_free(_verify_problem(n, c))]
+    assert len(free) >= 12, free
 
 
 def test_verify_tiny_config_full():
-    # The tiny verify workload exactly: 2 sequences, q_len 2, 16:1, BF16, 128-page pool.
+    # The tiny verify workload exactly: 2 sequences, q_len 2, 16:1, BF16,
+    # 128-page pool; at its own bound it runs without the plan.
     p = w.poison_unused(w.config("tiny_verify"))
+    assert _plan_free(p)
+    _check(p, what="tiny_verify/plan-free")
     for split in (0, 64, 4096):
-        _check(p, split=split, what=f"tiny_verify/split{split}")
+        _check(p, split=split, what=f"tiny_verify/split{split}/planned", max_kv_len=_planned_bound(p))
 
 
 def test_verify_zero_query_tokens_in_batch():
