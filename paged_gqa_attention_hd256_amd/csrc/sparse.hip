@@ -5,18 +5,20 @@
 // Work unit: one wave per (query token, kv head, block of 16 query heads of
 // that kv group).  The waves of a workgroup are independent -- each owns its
 // LDS region and never waits for another -- so the gather of one wave overlaps
-// the arithmetic of the others without workgroup barriers.
+// the arithmetic of the others without workgroup barriers.  When the kv head
+// count divides the XCD count, every workgroup of an XCD works on one kv head
+// (head_job), so an XCD's L2 holds one head's rows.
 //
 // Per wave, the selected entries are processed in chunks: the wave first
 // translates a chunk of the row's index list into physical token rows of the
 // pool (index -> block-table page -> page * page_size + slot; negative for an
-// entry that selects nothing) and keeps that table in LDS; then it streams
-// 16-key tiles of K and V through two LDS stages each
-// by 16-byte DMA whose per-lane source comes from the table, software
-// pipelined: the scores and softmax of tile i + 1 run between the requests
-// and the products of tile i's PV.  Because the table is read from LDS, no
-// vector-memory load sits between the DMA instructions and their counter can
-// be waited on exactly.
+// entry that selects nothing) and keeps that table in LDS (the chunk's indices
+// were requested before the previous chunk's copies); then it streams 16-key
+// tiles of K and V through two LDS stages each by 16-byte DMA whose per-lane
+// source comes from the table, software pipelined: the scores and softmax of
+// tile i + 1 run between the requests and the products of tile i's PV.
+// Because the table is read from LDS, no vector-memory load sits between the
+// DMA instructions and their counter can be waited on exactly.
 #include <algorithm>
 #include <type_traits>
 
