@@ -194,6 +194,28 @@ int paged_attn_verify_noalloc(const void* q, int32_t q_dtype, const float* q_des
                               int32_t max_q_len, int32_t max_kv_len, const pga_paged_kv* kv, float softmax_scale,
                               int32_t kv_split_tokens, void* out, float* lse, void* stream);
 
+/*
+ * Measurement helper: the page gather of paged_attn_verify alone, the
+ * practical bandwidth roof of that call on a given batch (SGLang PR #36330,
+ * Motivation: the speculative-verify cost is the KV pages each query group
+ * loads).  It runs the verify call's own work split and grid (the same
+ * num_seqs, lengths, host bounds, kv and kv_split_tokens give the same pieces
+ * and workgroups) and the same 16-byte non-temporal page copies into the same
+ * LDS tiles on the same pipeline, in one launch, and only adds up what it
+ * copies:
+ *   out[b * num_kv_heads + g] += sum over keys j < min(Lk_b, max_kv_len) of
+ *     every 32-bit word of K_j and of V_j of kv head g, mod 2^32
+ *   (nothing for sequences with no query token), an exact, order-independent
+ *   checksum when out starts at zero.
+ * The query heads do not change the split, so none are passed.
+ *   out  [num_seqs * num_kv_heads] uint32, 4-byte aligned, added into
+ * Returns PGA_OK or a PGA_ERR_* code (the argument checks of
+ * paged_attn_verify that apply).
+ */
+int paged_attn_verify_gather_sum(int32_t num_seqs, const int32_t* cu_seqlens_q, const int32_t* seq_lens_k,
+                                 int32_t max_q_len, int32_t max_kv_len, const pga_paged_kv* kv,
+                                 int32_t kv_split_tokens, uint32_t* out, void* stream);
+
 /* Workspace bytes paged_attn_verify needs for these host bounds.  A balanced
  * split can cut any history, so this is > 0 whenever the bounds admit any
  * work; 0 for bounds with no work (no sequences, max_kv_len 0) or invalid

@@ -20,7 +20,7 @@ import torch
 
 __all__ = [
     "PagedKV", "paged_attn_verify", "paged_attn_verify_noalloc", "paged_attn_prefill_prefix", "sparse_paged_attn",
-    "sparse_splits", "sparse_gather_sum", "sparse_workspace_bytes", "prefill_quantize_fp8", "quantize_workspace_bytes", "validate_inputs",
+    "sparse_splits", "sparse_gather_sum", "verify_gather_sum", "sparse_workspace_bytes", "prefill_quantize_fp8", "quantize_workspace_bytes", "validate_inputs",
     "verify_workspace_bytes", "verify_split_tokens", "status_string", "abi_version", "library_path",
     "PagedGQAError", "LibraryNotBuilt", "load_library",
 ]
@@ -87,6 +87,8 @@ def load_library():
             lib.sparse_paged_attn.restype = ctypes.c_int
             lib.sparse_gather_sum.argtypes = [I32, I32, P, P, P, I64, I32, KVP, P, P]
             lib.sparse_gather_sum.restype = ctypes.c_int
+            lib.paged_attn_verify_gather_sum.argtypes = [I32, P, P, I32, I32, KVP, I32, P, P]
+            lib.paged_attn_verify_gather_sum.restype = ctypes.c_int
             lib.sparse_paged_attn_splits.argtypes = [I32, I32, I32, I32]
             lib.sparse_paged_attn_splits.restype = I32
             lib.sparse_paged_attn_workspace_bytes.argtypes = [I32, I32, I32, I32]
@@ -313,6 +315,23 @@ def sparse_gather_sum(cu_seqlens_q, seq_lens_k, indices, kv: PagedKV, num_select
                                indices.data_ptr(), indices.stride(0), ns, ctypes.byref(s), out.data_ptr(),
                                _stream(stream))
     _check("sparse_gather_sum", st)
+    return out
+
+
+def verify_gather_sum(cu_seqlens_q, seq_lens_k, max_q_len: int, max_kv_len: int, kv: PagedKV,
+                      kv_split_tokens: int = 0, out=None, stream=None):
+    """Measurement helper: the page gather of ``paged_attn_verify`` on its own
+    work split (the K and V rows of every key below each history's length, per
+    kv head), summed as 32-bit words and added into uint32-valued int32
+    ``out`` [num_seqs, Hkv] (zeros when not given), which it returns."""
+    lib = load_library()
+    s = kv._struct()
+    if out is None:
+        out = torch.zeros((seq_lens_k.shape[0], kv.num_kv_heads), dtype=torch.int32, device=seq_lens_k.device)
+    st = lib.paged_attn_verify_gather_sum(seq_lens_k.shape[0], cu_seqlens_q.data_ptr(), seq_lens_k.data_ptr(),
+                                          int(max_q_len), int(max_kv_len), ctypes.byref(s), int(kv_split_tokens or 0),
+                                          out.data_ptr(), _stream(stream))
+    _check("paged_attn_verify_gather_sum", st)
     return out
 
 

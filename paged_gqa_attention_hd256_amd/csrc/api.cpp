@@ -238,6 +238,23 @@ int32_t paged_attn_verify_split_tokens(int32_t num_q_heads, int32_t num_kv_heads
 // partials go to the library's fixed per-device scratch, laid out for this
 // call exactly (partial rows in their stored width, slots for the actual
 // grid) and refused with PGA_ERR_SCRATCH when they do not fit.
+//
+// The grid of a verify call (and of its page-gather roof): the stream-K plan's
+// persistent grid, or for small calls one workgroup per tile of each unit with
+// no plan (at most as many slots as the plan's workspace holds, wg_cap >=
+// units * tiles).  Returns the plan-free mode's tiles per unit, 0 under the plan.
+static int32_t verify_grid(int32_t num_seqs, const pga_paged_kv* kv, int32_t max_kv_len, const VerifyPlan& p,
+                           int& num_wg) {
+  const int occupancy = kv->dtype == kFP8 ? 2 : 1;  // workgroups per CU the LDS allows
+  num_wg = std::max(1, std::min(p.wg_cap, device_cus() * occupancy));
+  const int64_t tiles_bound = cdiv(max_kv_len, kTileKeys);
+  const int64_t static_tiles = int64_t(num_seqs) * kv->num_kv_heads * tiles_bound;
+  if (tiles_bound > 0 && tiles_bound <= 64 && static_tiles <= pga::kVerifyStaticMaxTiles) {
+    num_wg = static_cast<int>(static_tiles);
+    return static_cast<int32_t>(tiles_bound);
+  }
+  return 0;
+}
 static int prepare_verify(const void* q, int32_t q_dtype, const float* q_descale, int32_t num_q_heads,
                           int32_t num_seqs, const int32_t* cu_seqlens_q, const int32_t* seq_lens_k, int32_t max_q_len,
                           int32_t max_kv_len, const pga_paged_kv* kv, float softmax_scale, int32_t kv_split_tokens,
@@ -256,14 +273,7 @@ static int prepare_verify(const void* q, int32_t q_dtype, const float* q_descale
   if (!aligned(q, 16) || !aligned(out, 8) || (lse && !aligned(lse, 4))) return PGA_ERR_UNSUPPORTED;
   if (int e = plan_verify(num_q_heads, kv->num_kv_heads, num_seqs, max_q_len, max_kv_len, kv_split_tokens, p))
     return e;
-  const int occupancy = kv->dtype == kFP8 ? 2 : 1;  // workgroups per CU the LDS allows
-  num_wg = std::max(1, std::min(p.wg_cap, device_cus() * occupancy));
-  // Small calls: one workgroup per tile of each unit, no plan (at most as many
-  // slots as the stream-K plan's workspace holds: wg_cap >= units * tiles).
-  const int64_t tiles_bound = cdiv(max_kv_len, kTileKeys);
-  const int64_t static_tiles = int64_t(num_seqs) * kv->num_kv_heads * tiles_bound;
-  const bool plan_free = tiles_bound > 0 && tiles_bound <= 64 && static_tiles <= pga::kVerifyStaticMaxTiles;
-  if (plan_free) num_wg = static_cast<int>(static_tiles);
+  const int32_t plan_free_tiles = verify_grid(num_seqs, kv, max_kv_len, p, num_wg);
   size_t ws_o_bytes = p.ws_o_bytes, ws_lse_bytes = p.ws_lse_bytes;
   if (use_scratch) {
     if (p.ws_bytes > 0) {
@@ -304,7 +314,7 @@ static int prepare_verify(const void* q, int32_t q_dtype, const float* q_descale
   a.ws_o = workspace;
   a.ws_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + ws_o_bytes);
   a.ws_plan = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + ws_o_bytes + ws_lse_bytes);
-  a.static_tiles = plan_free ? static_cast<int32_t>(tiles_bound) : 0;
+  a.static_tiles = plan_free_tiles;
   return PGA_OK;
 }
 
@@ -373,6 +383,38 @@ int paged_attn_verify_noalloc(const void* q, int32_t q_dtype, const float* q_des
   if (int e = launch_status(pga::launch_verify(a, kv->dtype, num_wg, s))) return e;
   if (a.static_tiles == 1) return PGA_OK;  // every unit fits one tile: all written directly
   return launch_status(pga::launch_verify_merge(a, kv->dtype, num_wg, s));
+}
+
+int paged_attn_verify_gather_sum(int32_t num_seqs, const int32_t* cu_seqlens_q, const int32_t* seq_lens_k,
+                                 int32_t max_q_len, int32_t max_kv_len, const pga_paged_kv* kv,
+                                 int32_t kv_split_tokens, uint32_t* out, void* stream) {
+  if (!cu_seqlens_q || !seq_lens_k || !out || !kv) return PGA_ERR_NULL;
+  if (num_seqs < 0 || max_kv_len < 0 || max_q_len < 1 || max_q_len > 4) return PGA_ERR_SHAPE;
+  if (int e = check_kv(kv, kv->num_kv_heads > 0 ? kv->num_kv_heads : 1,
+                       cdiv(max_kv_len, kv->page_size > 0 ? kv->page_size : 1)))
+    return e;
+  if (kv_split_tokens < 0 || kv_split_tokens % kTileKeys != 0) return PGA_ERR_SHAPE;
+  if (!aligned(out, 4)) return PGA_ERR_UNSUPPORTED;
+  // The work split does not depend on the query heads: plan as for one per kv head.
+  VerifyPlan p;
+  if (int e = plan_verify(kv->num_kv_heads, kv->num_kv_heads, num_seqs, max_q_len, max_kv_len, kv_split_tokens, p))
+    return e;
+  if (num_seqs == 0) return PGA_OK;
+  int num_wg = 0;
+  pga::VerifyArgs a{};
+  a.static_tiles = verify_grid(num_seqs, kv, max_kv_len, p, num_wg);
+  a.hq = kv->num_kv_heads;
+  a.r = 1;
+  a.num_seqs = num_seqs;
+  a.cu_q = cu_seqlens_q;
+  a.lens_k = seq_lens_k;
+  a.kv = make_kv(kv);
+  a.max_q_len = max_q_len;
+  a.max_kv_len = max_kv_len;
+  a.seg_tiles = p.seg_tiles;
+  a.rows_cap = p.rows_cap;
+  a.sum_out = out;
+  return launch_status(pga::launch_verify_gather(a, kv->dtype, num_wg, static_cast<hipStream_t>(stream)));
 }
 
 int paged_attn_prefill_prefix(const void* q, int32_t q_dtype, const float* q_descale, int32_t num_q_heads,

@@ -32,8 +32,6 @@
 
 namespace pga {
 
-typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
-
 // The sparse kernel's shape: waves per CU, rows per stage, table entries.
 template <int KV>
 struct GatherCfg {

@@ -63,6 +63,7 @@ struct VerifyArgs {
   int32_t* ws_plan;        // [units][2]: first tile, first segment of each unit; then tiles per workgroup
   int32_t static_tiles;    // > 0: plan-free mode, workgroup w takes tile w % static_tiles of unit
                            //   w / static_tiles and writes slot w (0: the stream-K plan)
+  uint32_t* sum_out;       // [units] checksums the page-gather roof adds into (verify_gather_kernel only)
 };
 
 // Prefill against a cached prefix: one workgroup per (tile of query tokens,
@@ -168,6 +169,7 @@ hipError_t verify_scratch(void** ptr);
 // Launchers (defined next to their kernels).  They return the launch status.
 hipError_t launch_verify(const VerifyArgs& a, int kv_dtype, int num_wg, hipStream_t s);
 hipError_t launch_verify_merge(const VerifyArgs& a, int kv_dtype, int num_wg, hipStream_t s);
+hipError_t launch_verify_gather(const VerifyArgs& a, int kv_dtype, int num_wg, hipStream_t s);
 // Query tokens per prefill workgroup for this dtype pair and group size r.
 int prefill_tile_tokens(int q_dtype, int kv_dtype, int r);
 hipError_t launch_prefill(const PrefillArgs& a, int q_dtype, int kv_dtype, int q_tiles, hipStream_t s);

@@ -178,10 +178,53 @@ __device__ __forceinline__ void verify_piece(const VerifyArgs& a, CausalSmem<KV,
   }
 }
 
+// The page-gather roof (verify_gather_kernel): the copies of one piece, on
+// the same pipeline, only summed.  Each lane adds the 32-bit words of the
+// 16-byte chunks it copied itself, of rows holding keys below k_hi (the last
+// tile's rows past it repeat key k_hi - 1).
 template <int KV>
-__global__ __launch_bounds__(256, (KV == kFP8) ? 2 : 1) void verify_kernel(VerifyArgs a) {
-  __shared__ CausalSmem<KV, 4> sm;
-  __shared__ int plan_lds[5];
+struct SumTile {
+  using G = TileGeom<KV>;
+  static constexpr int kRowsPerWave = 16;                       // 64 keys over 4 waves
+  static constexpr int kRowsPerDma = 1024 / G::kRowBytes;
+  static constexpr int kDma = kRowsPerWave / kRowsPerDma;
+  u32x4* acc;
+  int k_hi;
+  __device__ __forceinline__ void add(const lds_t* t, int tb) const {
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = lane_id();
+    u32x4 x[kDma];
+#pragma unroll
+    for (int u = 0; u < kDma; ++u)
+      x[u] = lds_load<u32x4>(t + (kRowsPerWave * w + u * kRowsPerDma) * G::kRowBytes + 16 * lane);
+#pragma unroll
+    for (int u = 0; u < kDma; ++u) {
+      const int row = kRowsPerWave * w + u * kRowsPerDma + lane / G::kChunks;
+      const unsigned m = tb + row < k_hi ? ~0u : 0u;
+      *acc += x[u] & u32x4{m, m, m, m};
+    }
+  }
+  __device__ __forceinline__ void front(const lds_t* kt, int tb) const { add(kt, tb); }
+  __device__ __forceinline__ void back(const lds_t* vt, int tb) const { add(vt, tb); }
+};
+
+// One piece of the roof: keys [k_lo, k_hi) of kv head g of sequence b, added
+// into sum_out[unit] (every word of every copied K and V row, mod 2^32).
+template <int KV>
+__device__ __forceinline__ void gather_piece(const VerifyArgs& a, CausalSmem<KV, 4>& sm, int b, int g, int k_lo,
+                                             int k_hi, int2 first) {
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  stream_keys<true>(sm, a.kv, a.kv.bt + (int64_t)b * a.kv.bt_stride, g, k_lo, k_hi, first, SumTile<KV>{&acc, k_hi});
+  uint32_t t = acc[0] + acc[1] + acc[2] + acc[3];
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) t += (uint32_t)__shfl_xor((int)t, off);
+  if (lane_id() == 0) atomicAdd(a.sum_out + (int64_t)b * a.kv.num_kv_heads + g, t);
+}
+
+// The work split and piece loop shared by the attention kernel and its
+// page-gather roof (SUM: the roof, which writes no workspace).
+template <int KV, bool SUM>
+__device__ __forceinline__ void verify_body(const VerifyArgs& a, CausalSmem<KV, 4>& sm, int* plan_lds) {
   const int wg = blockIdx.x, num_wg = gridDim.x;
   const int hkv = a.kv.num_kv_heads;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -207,8 +250,11 @@ __global__ __launch_bounds__(256, (KV == kFP8) ? 2 : 1) void verify_kernel(Verif
     const int tiles = (lq > 0 && lk > 0) ? (lk + 63) >> 6 : 0;
     if (k >= tiles) return;  // workgroup-uniform
     const int k_hi = min(64 * k + 64, lk);
-    verify_piece<KV>(a, sm, b, g, tok0, lq, lk, 64 * k, k_hi, int2{key0 < k_hi ? page : -1, 0}, tiles == 1,
-                     (int64_t)wg);
+    if constexpr (SUM)
+      gather_piece<KV>(a, sm, b, g, 64 * k, k_hi, int2{key0 < k_hi ? page : -1, 0});
+    else
+      verify_piece<KV>(a, sm, b, g, tok0, lq, lk, 64 * k, k_hi, int2{key0 < k_hi ? page : -1, 0}, tiles == 1,
+                       (int64_t)wg);
     return;
   }
 
@@ -239,7 +285,7 @@ __global__ __launch_bounds__(256, (KV == kFP8) ? 2 : 1) void verify_kernel(Verif
   int tu = tprefix * hkv + g * sw.span;   // start of unit (b, g) in the flattened list
   int su = sprefix * hkv + g * sw.segs;   // first segment of unit (b, g)
 
-  if (wg == 0 && threadIdx.x == 0) a.ws_plan[2 * a.num_seqs * hkv] = tpw;
+  if (!SUM && wg == 0 && threadIdx.x == 0) a.ws_plan[2 * a.num_seqs * hkv] = tpw;
   int cur = t0;
   while (cur < t1) {
     // Segment s of the unit occupies [s * S, s * S + kSegStartCost + its tiles)
@@ -257,7 +303,7 @@ __global__ __launch_bounds__(256, (KV == kFP8) ? 2 : 1) void verify_kernel(Verif
     const int lt0 = s * a.seg_tiles + (xr - s * S - kSegStartCost);
     const int lt1 = s * a.seg_tiles + (xe - s * S - kSegStartCost);
     const int lts1 = s * a.seg_tiles + seg_tiles;
-    if (lt0 == 0 && threadIdx.x == 0) {  // this workgroup holds the unit's first tile: record where it lies
+    if (!SUM && lt0 == 0 && threadIdx.x == 0) {  // this workgroup holds the unit's first tile: record where it lies
       a.ws_plan[2 * (b * hkv + g)] = tu;
       a.ws_plan[2 * (b * hkv + g) + 1] = su;
     }
@@ -269,8 +315,11 @@ __global__ __launch_bounds__(256, (KV == kFP8) ? 2 : 1) void verify_kernel(Verif
     // A run that covers a whole uncut unit writes the output; any other piece
     // writes its partial rows to its workspace slot.
     const bool direct = lt0 == s * a.seg_tiles && lt1 == lts1 && sw.segs == 1;
-    verify_piece<KV>(a, sm, b, g, tok0, lq, lk, k_lo, k_hi, first_pages<4>(a.kv, bt_row, k_lo, k_hi), direct,
-                     (int64_t)su + s + wg);
+    if constexpr (SUM)
+      gather_piece<KV>(a, sm, b, g, k_lo, k_hi, first_pages<4>(a.kv, bt_row, k_lo, k_hi));
+    else
+      verify_piece<KV>(a, sm, b, g, tok0, lq, lk, k_lo, k_hi, first_pages<4>(a.kv, bt_row, k_lo, k_hi), direct,
+                       (int64_t)su + s + wg);
     cur = tu + xe;
     if (xe == sw.span) {  // next unit: next kv head, or the next sequence with work
       tu += sw.span;
@@ -285,6 +334,23 @@ __global__ __launch_bounds__(256, (KV == kFP8) ? 2 : 1) void verify_kernel(Verif
       }
     }
   }
+}
+
+template <int KV>
+__global__ __launch_bounds__(256, (KV == kFP8) ? 2 : 1) void verify_kernel(VerifyArgs a) {
+  __shared__ CausalSmem<KV, 4> sm;
+  __shared__ int plan_lds[5];
+  verify_body<KV, false>(a, sm, plan_lds);
+}
+
+// The same work split, grid and copies as verify_kernel, with the arithmetic
+// replaced by a checksum of the copied rows: the rate the page gather alone
+// reaches on a call's pages (measurement only).
+template <int KV>
+__global__ __launch_bounds__(256, (KV == kFP8) ? 2 : 1) void verify_gather_kernel(VerifyArgs a) {
+  __shared__ CausalSmem<KV, 4> sm;
+  __shared__ int plan_lds[5];
+  verify_body<KV, true>(a, sm, plan_lds);
 }
 
 // Log-sum-exp merge of the partial rows of every (sequence, kv head) unit that
@@ -484,6 +550,14 @@ hipError_t launch_verify(const VerifyArgs& a, int kv_dtype, int num_wg, hipStrea
     hipLaunchKernelGGL(verify_kernel<kFP8>, dim3(num_wg), dim3(256), 0, s, a);
   else
     hipLaunchKernelGGL(verify_kernel<kBF16>, dim3(num_wg), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_verify_gather(const VerifyArgs& a, int kv_dtype, int num_wg, hipStream_t s) {
+  if (kv_dtype == kFP8)
+    hipLaunchKernelGGL(verify_gather_kernel<kFP8>, dim3(num_wg), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(verify_gather_kernel<kBF16>, dim3(num_wg), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -309,3 +309,21 @@ def test_gather_rejects_pools_its_offsets_cannot_address(lib):
     assert gather(lib, kv=kv_struct(num_pages=(1 << 20) + 1)) == EUNSUP
     assert gather(lib, kv=kv_struct(k_stride_token=1 << 24, k_stride_page=16 << 24)) == EUNSUP
     assert gather(lib, kv=kv_struct(num_pages=1 << 20, k_stride_token=1 << 13, k_stride_page=16 << 13)) == EUNSUP
+
+
+def verify_gather(lib, kv=None, **kw):
+    a = dict(nseq=2, cuq=P(16384), lk=P(16384 + 64), maxq=4, maxk=1000, split=0, out=P(20480))
+    a.update(kw)
+    kv = kv or kv_struct()
+    return lib.paged_attn_verify_gather_sum(a["nseq"], a["cuq"], a["lk"], a["maxq"], a["maxk"], ctypes.byref(kv),
+                                            a["split"], a["out"], None)
+
+
+def test_verify_gather_rejects_invalid_arguments(lib):
+    assert verify_gather(lib, nseq=0) == OK
+    assert verify_gather(lib, out=None) == ENULL
+    assert verify_gather(lib, cuq=None) == ENULL
+    assert verify_gather(lib, maxq=5) == ESHAPE
+    assert verify_gather(lib, split=10) == ESHAPE
+    assert verify_gather(lib, out=P(20481)) == EUNSUP
+    assert verify_gather(lib, kv=kv_struct(block_table_stride=10)) == ESHAPE  # fewer columns than the bound's pages

@@ -69,3 +69,60 @@ def test_gather_sum_exact(name, c):
     assert got.shape == exp.shape
     bad = np.argwhere(got != exp)
     assert bad.size == 0, f"{name}: {len(bad)} sums differ, first at {bad[:3].tolist()}"
+
+
+# ---------------------------------------------------------------------------
+# The page-gather roof of the verify call (paged_attn_verify_gather_sum): per
+# (sequence, kv head), the word sum of the K and V rows of every key below the
+# history's length (none for a sequence without query tokens), exact.
+
+def _expected_verify(p, max_kv_len) -> np.ndarray:
+    k = np.ascontiguousarray(p.k_cache).view(np.uint32)
+    v = np.ascontiguousarray(p.v_cache).view(np.uint32)
+    lq = np.diff(p.cu_seqlens_q)
+    out = np.zeros((len(p.seq_lens_k), p.num_kv_heads), dtype=np.uint64)
+    for b, lk in enumerate(p.seq_lens_k):
+        lk = min(int(lk), max_kv_len)
+        if lq[b] <= 0 or lk <= 0:
+            continue
+        j = np.arange(lk)
+        pages = p.block_table[b, j // p.page_size]
+        slots = j % p.page_size
+        if p.kv_layout == "NHD":
+            rows = k[pages, slots].astype(np.uint64) + v[pages, slots].astype(np.uint64)  # [n, hkv, nw]
+        else:
+            rows = k[pages, :, slots].astype(np.uint64) + v[pages, :, slots].astype(np.uint64)
+        out[b] = rows.sum(axis=(0, 2))
+    return (out % (1 << 32)).astype(np.uint32)
+
+
+VERIFY_CASES = [
+    ("fp8_16to1", dict(seed=[111], lq=[4, 4, 2, 3], lk=[700, 65, 1500, 2049], hq=16, hkv=1, kv=w.FP8)),
+    ("bf16_32to2", dict(seed=[112], lq=[3, 3], lk=[513, 1300], hq=32, hkv=2, kv=w.BF16)),
+    ("fp8_hnd_page64", dict(seed=[113], lq=[2, 1], lk=[901, 64], hq=16, hkv=2, kv=w.FP8, layout="HND", page=64)),
+    ("fp8_zero_q_tokens", dict(seed=[114], lq=[2, 0, 3], lk=[100, 50, 300], hq=16, hkv=1, kv=w.FP8)),
+]
+
+
+@pytest.mark.parametrize("name,c", VERIFY_CASES, ids=[n for n, _ in VERIFY_CASES])
+@pytest.mark.parametrize("plan", ["exact_bound", "planned_64", "planned_0"])
+def test_verify_gather_sum_exact(name, c, plan):
+    import torch
+
+    import paged_gqa_attention_hd256_amd as pga
+    from paged_gqa_attention_hd256_amd import problem_io
+
+    p = w.make_causal(name, c["seed"], c["lq"], c["lk"], c["hq"], c["hkv"], kv_dtype=c["kv"],
+                      page_size=c.get("page", 16), layout=c.get("layout", "NHD"), mode="verify")
+    p = w.poison_unused(p)
+    mk = int(np.max(p.seq_lens_k)) if plan == "exact_bound" else 64 * 65  # past 64 tiles: the planned split
+    split = 64 if plan == "planned_64" else 0
+    print(f"case {name} {plan}", flush=True)
+    dp = problem_io.to_device(p, max_kv_len=mk)
+    got = pga.verify_gather_sum(dp.cu_seqlens_q, dp.seq_lens_k, max(1, int(np.diff(p.cu_seqlens_q).max())), mk,
+                                dp.kv, kv_split_tokens=split)
+    torch.cuda.synchronize()
+    got = got.cpu().numpy().view(np.uint32)
+    exp = _expected_verify(p, mk)
+    bad = np.argwhere(got != exp)
+    assert bad.size == 0, f"{name}/{plan}: {len(bad)} sums differ, first at {bad[:3].tolist()}"
