@@ -103,20 +103,28 @@ __global__ __launch_bounds__(kQuantThreads) void quant_amax_kernel(const uint4* 
 // comment).  FAST is the reciprocal scheme, valid for d in [2^-64, 2^64]; it
 // is exact up to the saturation point, beyond which only |y| > 448 matters,
 // and q0 is clamped so that no infinity meets a zero.
+// One correction of the estimate q0 of x / d: y = q0 - e r with the remainder
+// e = q0 d - x formed exactly by an fma (the negation of x - q0 d, so y is
+// the usual q0 + (x - q0 d) r bit for bit).  Written this way round, a zero
+// quotient keeps its sign without a copysign: for x = -0, q0 = -0, e = +0 and
+// y = -0 - (+0) r = -0.  The correction never changes the sign of a nonzero q0.
+__device__ __forceinline__ float correct_quotient(float x, float q0, float d, float r) {
+  const float e = __builtin_fmaf(q0, d, -x);
+  return __builtin_fmaf(-e, r, q0);
+}
+
 template <bool FAST>
 struct Divider {
   float d, r;
   __device__ __forceinline__ explicit Divider(float descale) : d(descale), r(1.0f / descale) {}
+  __device__ __forceinline__ float correct(float x, float q0) const { return correct_quotient(x, q0, d, r); }
   __device__ __forceinline__ float operator()(float x) const {
     if constexpr (!FAST) {
       return x / d;
     } else {
       float q0 = __fmul_rn(x, r);
       q0 = __builtin_fminf(__builtin_fmaxf(q0, -1024.0f), 1024.0f);
-      const float e = __builtin_fmaf(-q0, d, x);
-      // The correction never changes the sign of a nonzero q0; copying q0's
-      // sign keeps the sign of a zero quotient (-0 / d is -0, but e is +0).
-      return __builtin_copysignf(__builtin_fmaf(e, r, q0), q0);
+      return correct(x, q0);
     }
   }
 };
@@ -137,11 +145,7 @@ __device__ __forceinline__ float clamp448(float y) {
 struct DynamicDivider {
   float d, r;
   __device__ __forceinline__ explicit DynamicDivider(float descale) : d(descale), r(1.0f / descale) {}
-  __device__ __forceinline__ float operator()(float x) const {
-    const float q0 = __fmul_rn(x, r);
-    const float e = __builtin_fmaf(-q0, d, x);
-    return __builtin_copysignf(__builtin_fmaf(e, r, q0), q0);
-  }
+  __device__ __forceinline__ float operator()(float x) const { return correct_quotient(x, __fmul_rn(x, r), d, r); }
 };
 
 // Eight bf16 values -> eight E4M3FN codes (little-endian in the result).
