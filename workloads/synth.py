@@ -340,6 +340,13 @@ _CONFIGS = {
     "sparse_fp8": 5,
     "sparse_fp8_260rows": 6,
     "prefill_quant_32k": 7,
+    # The shapes beyond the five named workloads: q_len 1, other GQA ratios,
+    # bf16 prefill, a 64-token page in the head-major layout.
+    "verify_decode_fp8": 8,
+    "mtp_verify_fp8_6to1": 9,
+    "sparse_fp8_3to1": 10,
+    "prefix_prefill_32k_bf16": 11,
+    "prefix_prefill_32k_page64_hnd": 12,
 }
 
 
@@ -382,6 +389,25 @@ def config(name: str) -> Problem:
         # The few-row regime of the same selection: the last 260 rows of the
         # 32768-token sequence, 24 q / 2 kv, 2051 selected tokens each, FP8 K/V.
         return make_sparse(name, [c, 0], [260], [32768], 24, 2, 2051, kv_dtype=FP8)
+    if name in ("verify_decode_fp8", "mtp_verify_fp8_6to1"):
+        # The FP8 verify batch (64 sequences, KV lengths uniform in [2048, 32768])
+        # as plain decode (q_len 1, 16 q / 1 kv) and at 6 q / 1 kv (q_len 4).
+        rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([c, 0]).spawn(6)[0]))
+        lens_k = rng.integers(2048, 32768, size=64, endpoint=True)
+        lq, hq = (1, 16) if name == "verify_decode_fp8" else (4, 6)
+        return make_causal(name, [c, 0], [lq] * 64, lens_k, hq, 1, kv_dtype=FP8, q_dtype=BF16,
+                           kv_sigma=0.5, mode="verify")
+    if name == "sparse_fp8_3to1":
+        # The sparse selection at 3 q / 1 kv (24 q / 8 kv heads split eight ways):
+        # 8192 rows at positions 24576..32767, 2051 selected tokens each, FP8 K/V.
+        return make_sparse(name, [c, 0], [8192], [32768], 3, 1, 2051, kv_dtype=FP8)
+    if name == "prefix_prefill_32k_bf16":
+        # The 16k-new / 32k-context prefill in bf16 (Q, K and V).
+        return make_causal(name, [c, 0], [16384], [32768], 8, 1, kv_dtype=BF16, q_dtype=BF16, mode="prefill")
+    if name == "prefix_prefill_32k_page64_hnd":
+        # The FP8 16k / 32k prefill over 64-token pages laid out [pages, heads, slots, d].
+        return make_causal(name, [c, 0], [16384], [32768], 8, 1, kv_dtype=FP8, q_dtype=FP8, page_size=64,
+                           layout="HND", mode="prefill")
     if name in ("sparse_bf16", "sparse_fp8"):
         # 8192 query rows at positions 24576..32767 of one 32768-token sequence, 24 q / 2 kv,
         # 2051 selected tokens per row; the same draws encoded as BF16 or FP8 K/V.
