@@ -8,9 +8,9 @@
 // kernel, with no gather to contiguous memory first (ROCm/ATOM PR #2830, recipe
 // commit).  Workgroups are ordered longest first.
 //
-// FP8 queries with FP8 keys (the pages' FP8 FMHA) run the warp-specialised
-// prefill_ws_kernel below; bf16 queries run prefill_kernel, the tile step
-// shared with verify.
+// FP8 queries with FP8 keys (the pages' FP8 FMHA) and bf16 queries with bf16
+// keys run the warp-specialised prefill_ws_kernel below; bf16 queries against
+// FP8 keys run prefill_kernel, the tile step shared with verify.
 #include <type_traits>
 
 #include "causal_stream.h"
@@ -73,7 +73,9 @@ __global__ __launch_bounds__(64 * NW, KV == kFP8 ? 2 : 1) void prefill_kernel(Pr
 }
 
 // ---------------------------------------------------------------------------
-// FP8 queries and keys: a warp-specialised, software-pipelined tile loop.
+// Queries and keys of one encoding (FP8 and FP8, or bf16 and bf16): a
+// warp-specialised, software-pipelined tile loop.  Tiles hold 64 FP8 or 32
+// bf16 keys (16 KB of K and of V either way).
 //
 // The tile step above runs a tile's QK^T, softmax and PV back to back in every
 // wave, so a wave's vector work (scaling, maxima, exponentials, conversions)
@@ -81,7 +83,7 @@ __global__ __launch_bounds__(64 * NW, KV == kFP8 ? 2 : 1) void prefill_kernel(Pr
 // (128 rows, one workgroup per CU) split by kind of work:
 //  - waves 0 .. 3 compute scores and softmax, wave w for rows 32 w .. 32 w + 31
 //    (two 16-row blocks sharing every K fragment read from LDS), and issue
-//    every tile copy (16 rows of each K and V tile per wave);
+//    every tile copy (a quarter of the rows of each K and V tile per wave);
 //  - waves 4 .. 7 compute the PV product, wave 4 + d for head dims
 //    64 d .. 64 d + 63 of all 128 rows.
 // Each SIMD holds one wave of each kind, so the softmax's vector work runs
@@ -94,20 +96,37 @@ __global__ __launch_bounds__(64 * NW, KV == kFP8 ? 2 : 1) void prefill_kernel(Pr
 // next copies fill.
 constexpr int kPipeStages = 3;
 constexpr int kPipeRows = 128;  // query rows per workgroup
+// Keys per tile: 64 FP8 keys, 32 bf16 keys -- the same 16 KB of K (and of V)
+// per stage, so three stages of both fit LDS with the probabilities.
+template <int KV>
+constexpr int kWsKeys = KV == kFP8 ? 64 : 32;
 
-template <int NRB>
-struct PipeSmem {
-  static constexpr int kTile = TileGeom<kFP8>::tile_bytes<64>();
-  char k[kPipeStages][kTile];
-  char v[kPipeStages][kTile];
-  Exchange<kFP8, NRB> x[2];
+// Probabilities of one tile for the PV waves: per row block, 32-key step and
+// part (fp16 P; bf16 P as a high and a low part), the B operand of each lane;
+// the rows' rescale factors, and per row block whether any row was rescaled.
+template <int KV, int NRB>
+struct WsExchange {
+  static constexpr int kSteps = kWsKeys<KV> / 32;
+  static constexpr int kPVec = KV == kFP8 ? 1 : 2;
+  i32x4 p[NRB][kSteps][kPVec][64];
+  float row[16 * NRB];
+  int grow[NRB];
 };
 
-// Copies of this wave's rows of one 64-key tile of K or V (global -> LDS).
-template <int NW>
+template <int KV, int NRB>
+struct PipeSmem {
+  static constexpr int kTile = TileGeom<KV>::template tile_bytes<kWsKeys<KV>>();
+  char k[kPipeStages][kTile];
+  char v[kPipeStages][kTile];
+  WsExchange<KV, NRB> x[2];
+};
+
+// Copies of this wave's rows of one tile of K or V (global -> LDS).
+template <int KV, int NW>
 struct TileCopy {
-  using G = TileGeom<kFP8>;
-  static constexpr int kRowsPerWave = 64 / NW;
+  using G = TileGeom<KV>;
+  static constexpr int kKeys = kWsKeys<KV>;
+  static constexpr int kRowsPerWave = kKeys / NW;
   static constexpr int kRowsPerDma = 1024 / G::kRowBytes;
   static constexpr int kDma = kRowsPerWave / kRowsPerDma;
   static_assert(kDma * kRowsPerDma == kRowsPerWave, "whole DMA instructions per wave");
@@ -129,9 +148,9 @@ struct TileCopy {
     }
   }
   // Page holding this wave's rows of tile `it` (keys from 0), read through the
-  // scalar cache; all of them lie in one page.
+  // scalar cache; all of them lie in one page (pages hold at least 16 keys).
   __device__ __forceinline__ int page(int it) const {
-    const int key0 = it * 64 + kRowsPerWave * w;
+    const int key0 = it * kKeys + kRowsPerWave * w;
     const int pidx = __builtin_amdgcn_readfirstlane(min(key0, k_hi - 1) >> kv.page_shift);
     return scalar_load(bt_row + pidx);
   }
@@ -140,7 +159,7 @@ struct TileCopy {
   __device__ __forceinline__ void issue(int it, int page, bool is_v, unsigned dst) const {
     const uint8_t* base = is_v ? kv.v : kv.k;
     const int64_t sh = is_v ? kv.v_sh : kv.k_sh, sp = is_v ? kv.v_sp : kv.k_sp, st = is_v ? kv.v_st : kv.k_st;
-    const int tb = it * 64;
+    const int tb = it * kKeys;
     const unsigned pmask = kv.page_size - 1;
     const bool page_ok = page >= 0 && page < kv.num_pages;
     const uint64_t pbase = page_ok ? (uint64_t)(uintptr_t)(base + g * sh + (int64_t)page * sp)
@@ -148,7 +167,7 @@ struct TileCopy {
     if (!page_ok) {
 #pragma unroll
       for (int u = 0; u < kDma; ++u) dma16_off(pbase, 0u, dst + (kRowsPerWave * w + u * kRowsPerDma) * G::kRowBytes);
-    } else if (tb + 64 <= k_hi) {
+    } else if (tb + kKeys <= k_hi) {
       const uint64_t tbase = pbase + (uint64_t)((tb & pmask) * (unsigned)st);
 #pragma unroll
       for (int u = 0; u < kDma; ++u)
@@ -175,7 +194,7 @@ struct TileCopy {
 // block's running row sums from an all-ones A operand.
 template <bool MASKED, int NRB>
 __device__ __forceinline__ void softmax_ws(RowStat& rs, f32x4& lsum, f32x4 (&s)[4], float c2, int lim,
-                                           Exchange<kFP8, NRB>& x, int rb) {
+                                           WsExchange<kFP8, NRB>& x, int rb) {
   const int lane = lane_id();
   const int gq = lane >> 4, n = lane & 15;
   float mt = kNegInf;
@@ -211,7 +230,7 @@ __device__ __forceinline__ void softmax_ws(RowStat& rs, f32x4& lsum, f32x4 (&s)[
 // PV of one tile for head dims 64 d .. 64 d + 63 of all NRB row blocks, after
 // rescaling the rows whose maximum moved.
 template <int NRB>
-__device__ __forceinline__ void pv_ws(f32x4 (&o)[4 * NRB], const lds_t* vt, const Exchange<kFP8, NRB>& x, int d) {
+__device__ __forceinline__ void pv_ws(f32x4 (&o)[4 * NRB], const lds_t* vt, const WsExchange<kFP8, NRB>& x, int d) {
   using G = TileGeom<kFP8>;
   const int lane = lane_id();
   const int gq = lane >> 4, sl = lane & 15;
@@ -256,9 +275,124 @@ __device__ __forceinline__ void pv_ws(f32x4 (&o)[4 * NRB], const lds_t* vt, cons
   }
 }
 
+// bf16 queries and keys, 32-key tiles.  Scores of the wave's NRB row blocks:
+// each K fragment read from LDS feeds one bf16 MFMA per row block.
+template <int NRB, int NMB>
+__device__ __forceinline__ void tile_scores_rows_bf16(const lds_t* kt, const QFragT<kBF16> (&qf)[NRB],
+                                                      f32x4 (&s)[NRB][NMB]) {
+  using G = TileGeom<kBF16>;
+  const int lane = lane_id();
+  const int n = lane & 15, gq = lane >> 4;
+#pragma unroll
+  for (int rb = 0; rb < NRB; ++rb)
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb) s[rb][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) {
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb) {
+      const bf16x8 k8 = lds_load<bf16x8>(kt + G::off(mb * 16 + n, 4 * ks + gq));
+#pragma unroll
+      for (int rb = 0; rb < NRB; ++rb) s[rb][mb] = mfma_bf16(k8, qf[rb].q[ks], s[rb][mb]);
+    }
+  }
+}
+
+// softmax_ws on a 32-key tile of bf16 keys: the probabilities are published as
+// a bf16 high and low part (keys 4 (lane / 16) + i and 16 + 4 (lane / 16) + i,
+// the B-operand order of the 32-key step), and the row sums count both parts.
+template <bool MASKED, int NRB>
+__device__ __forceinline__ void softmax_ws_bf16(RowStat& rs, f32x4& lsum, f32x4 (&s)[2], float c2, int lim,
+                                                WsExchange<kBF16, NRB>& x, int rb) {
+  const int lane = lane_id();
+  const int gq = lane >> 4, n = lane & 15;
+  float mt = kNegInf;
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if constexpr (MASKED) s[mb][i] = (mb * 16 + 4 * gq + i <= lim) ? s[mb][i] : kNegInf;
+      mt = fmaxf(mt, s[mb][i]);
+    }
+  mt = group4_max(mt);
+  mt = mt == kNegInf ? kNegInf : mt * c2;
+  const bool grow = __builtin_amdgcn_ballot_w64(mt > rs.m + kRescaleLog2) != 0;  // wave-uniform
+  const float m_new = grow ? fmaxf(rs.m, mt) : rs.m;
+  const float alpha = m_new == rs.m ? 1.f : fast_exp2(rs.m - m_new);
+  rs.m = m_new;
+  const float nm = m_new == kNegInf ? 0.f : -m_new;
+  x.row[16 * rb + n] = alpha;
+  x.grow[rb] = grow;
+  lsum *= alpha;
+  bf16x8 ph, pl;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const float v = fast_exp2(__builtin_fmaf(s[j >> 2][j & 3], c2, nm));
+    const __bf16 h = (__bf16)v;
+    ph[j] = h;
+    pl[j] = (__bf16)(v - (float)h);
+  }
+  x.p[rb][0][0][lane] = __builtin_bit_cast(i32x4, ph);
+  x.p[rb][0][1][lane] = __builtin_bit_cast(i32x4, pl);
+  const bf16x8 ones = {(__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f,
+                       (__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f};
+  lsum = mfma_bf16(ones, ph, lsum);
+  lsum = mfma_bf16(ones, pl, lsum);
+}
+
+// pv_ws on a 32-key tile of bf16 values: V^T by 16-bit transpose reads (lane
+// sl = 4e + q points at key 4 (lane / 16) + e, or 16 more, columns 4q .. 4q + 3
+// of the d-block), two bf16 products per block (high and low part of P).
+template <int NRB>
+__device__ __forceinline__ void pv_ws_bf16(f32x4 (&o)[4 * NRB], const lds_t* vt, const WsExchange<kBF16, NRB>& x,
+                                           int d) {
+  using G = TileGeom<kBF16>;
+  const int lane = lane_id();
+  const int gq = lane >> 4, sl = lane & 15;
+  int any = 0;
+#pragma unroll
+  for (int i = 0; i < NRB; ++i) any |= x.grow[i];
+  const int e = sl >> 2, q = sl & 3;
+  bf16x8 av[4];
+  i32x4 ph[NRB], pl[NRB];
+#pragma unroll
+  for (int db = 0; db < 4; ++db) {
+    const int chunk = 2 * (4 * d + db) + (q >> 1);
+    const i32x2 k0 = __builtin_bit_cast(i32x2, lds_tr16(vt + G::off(4 * gq + e, chunk) + 8 * (q & 1)));
+    const i32x2 k1 = __builtin_bit_cast(i32x2, lds_tr16(vt + G::off(16 + 4 * gq + e, chunk) + 8 * (q & 1)));
+    av[db] = __builtin_bit_cast(bf16x8, i32x4{k0[0], k0[1], k1[0], k1[1]});
+  }
+#pragma unroll
+  for (int rb = 0; rb < NRB; ++rb) {
+    ph[rb] = x.p[rb][0][0][lane];
+    pl[rb] = x.p[rb][0][1][lane];
+  }
+  asm volatile("" ::: "memory");
+  if (__builtin_amdgcn_readfirstlane(any) != 0) {
+#pragma unroll
+    for (int i = 0; i < 4 * NRB; ++i) asm volatile("" : "+v"(o[i]));
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) {
+      const float al = x.row[16 * rb + sl];
+#pragma unroll
+      for (int db = 0; db < 4; ++db) o[4 * rb + db] *= al;
+    }
+  }
+#pragma unroll
+  for (int rb = 0; rb < NRB; ++rb) {
+    const bf16x8 h = __builtin_bit_cast(bf16x8, ph[rb]), l = __builtin_bit_cast(bf16x8, pl[rb]);
+#pragma unroll
+    for (int db = 0; db < 4; ++db) o[4 * rb + db] = mfma_bf16(av[db], h, o[4 * rb + db]);
+#pragma unroll
+    for (int db = 0; db < 4; ++db) o[4 * rb + db] = mfma_bf16(av[db], l, o[4 * rb + db]);
+  }
+}
+
+template <int KV>
 __global__ __launch_bounds__(512, 1) void prefill_ws_kernel(PrefillArgs a) {
   constexpr int NRB = kPipeRows / 16;  // row blocks of the workgroup
-  __shared__ PipeSmem<NRB> sm;
+  constexpr int TK = kWsKeys<KV>;      // keys per tile
+  __shared__ PipeSmem<KV, NRB> sm;
   const int g = blockIdx.y, b = blockIdx.z;
   const int tok0 = a.cu_q[b];
   const int lq = min(a.cu_q[b + 1] - tok0, a.max_q_len);
@@ -287,18 +421,18 @@ __global__ __launch_bounds__(512, 1) void prefill_ws_kernel(PrefillArgs a) {
   const int lane = lane_id();
   const int n = lane & 15;
   const int32_t* bt_row = a.kv.bt + (int64_t)b * a.kv.bt_stride;
-  const int T = (k_hi + 63) >> 6;
-  constexpr unsigned kTile = PipeSmem<NRB>::kTile;
+  const int T = (k_hi + TK - 1) / TK;
+  constexpr unsigned kTile = PipeSmem<KV, NRB>::kTile;
 
   if (w < 4) {
     // ---- scores and softmax of row blocks 2w, 2w + 1; all tile copies ----
     // The four softmax waves copy 16 rows each of every K and V tile, so the
     // PV waves carry no copies, scalar loads or copy waits.
-    TileCopy<4> cp(a.kv, bt_row, g, k_hi);
+    TileCopy<KV, 4> cp(a.kv, bt_row, g, k_hi);
     int pg0 = cp.page(0), pg1 = T > 1 ? cp.page(1) : 0, pg2 = T > 2 ? cp.page(2) : 0;
     const unsigned kbuf = (unsigned)(uintptr_t)(lds_t*)&sm.k[0][0];
     const unsigned vbuf = (unsigned)(uintptr_t)(lds_t*)&sm.v[0][0];
-    constexpr int kDma = TileCopy<4>::kDma;
+    constexpr int kDma = TileCopy<KV, 4>::kDma;
     // Prologue copies: K and V of tiles 0 and 1, K of tile 2.
     cp.issue(0, pg0, false, kbuf);
     cp.issue(0, pg0, true, vbuf);
@@ -322,22 +456,28 @@ __global__ __launch_bounds__(512, 1) void prefill_ws_kernel(PrefillArgs a) {
       pg2 = pg3;
       pg3 = i + 4 < T ? cp.page(i + 4) : 0;
     };
-    QFragT<kFP8> qf[2];
+    QFragT<KV> qf[2];
     int klim[2];
     float c2 = a.c2_base * load_scale(a.q_ds) * load_scale(a.kv.k_ds);
-    const bool flip = c2 < 0.f;  // keep c2 positive: negate the queries instead (sign bit of every FP8 code)
+    const bool flip = c2 < 0.f;  // keep c2 positive: negate the queries instead (the sign bit of every element)
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int rr = 16 * (2 * w + j) + n;
       const bool ok = rr < rows;
       const int t2 = ok ? rr / a.r : 0;
-      load_q<kFP8, kFP8>(qf[j], a.q, tok0 + t_lo + t2, a.hq, g * a.r + (ok ? rr - t2 * a.r : 0), ok);
+      load_q<KV, KV>(qf[j], a.q, tok0 + t_lo + t2, a.hq, g * a.r + (ok ? rr - t2 * a.r : 0), ok);
       klim[j] = ok ? min(lk - lq + t_lo + t2, k_hi - 1) : -1;
       if (flip) {
+        if constexpr (KV == kFP8) {
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
+          for (int h = 0; h < 2; ++h)
 #pragma unroll
-          for (int i = 0; i < 8; ++i) qf[j].hi[h][i] ^= (int)0x80808080u;
+            for (int i = 0; i < 8; ++i) qf[j].hi[h][i] ^= (int)0x80808080u;
+        } else {
+#pragma unroll
+          for (int ks = 0; ks < 8; ++ks)
+            qf[j].q[ks] = __builtin_bit_cast(bf16x8, __builtin_bit_cast(i32x4, qf[j].q[ks]) ^ (int)0x80008000u);
+        }
       }
     }
     c2 = fmaxf(fabsf(c2), 1e-30f);  // a zero scale: every score counts the same
@@ -350,22 +490,30 @@ __global__ __launch_bounds__(512, 1) void prefill_ws_kernel(PrefillArgs a) {
       lsum[j] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
     auto tile = [&](int j, auto masked) {
-      f32x4 s[2][4];
-      tile_scores_rows<2, 4>((const lds_t*)&sm.k[0][0] + (j % kPipeStages) * kTile, qf, s);
-      Exchange<kFP8, NRB>& x = sm.x[j & 1];
+      f32x4 s[2][TK / 16];
+      const lds_t* kt = (const lds_t*)&sm.k[0][0] + (j % kPipeStages) * kTile;
+      WsExchange<KV, NRB>& x = sm.x[j & 1];
+      if constexpr (KV == kFP8) {
+        tile_scores_rows<2, 4>(kt, qf, s);
 #pragma unroll
-      for (int r = 0; r < 2; ++r)
-        softmax_ws<decltype(masked)::value>(rs[r], lsum[r], s[r], c2, klim[r] - 64 * j, x, 2 * w + r);
+        for (int r = 0; r < 2; ++r)
+          softmax_ws<decltype(masked)::value>(rs[r], lsum[r], s[r], c2, klim[r] - TK * j, x, 2 * w + r);
+      } else {
+        tile_scores_rows_bf16<2, 2>(kt, qf, s);
+#pragma unroll
+        for (int r = 0; r < 2; ++r)
+          softmax_ws_bf16<decltype(masked)::value>(rs[r], lsum[r], s[r], c2, klim[r] - TK * j, x, 2 * w + r);
+      }
     };
     wait_vmcnt<0>();
     barrier();
-    if (63 > min_lim)
+    if (TK - 1 > min_lim)
       tile(0, std::true_type{});
     else
       tile(0, std::false_type{});
     // Tiles needing the mask form a suffix, so two loops with one body each.
     int i = 0;
-    for (; i + 1 < T && 64 * (i + 1) + 63 <= min_lim; ++i) {
+    for (; i + 1 < T && TK * (i + 1) + TK - 1 <= min_lim; ++i) {
       open_step(i);
       tile(i + 1, std::false_type{});
     }
@@ -376,7 +524,7 @@ __global__ __launch_bounds__(512, 1) void prefill_ws_kernel(PrefillArgs a) {
     open_step(T - 1);
     // Row sums for the PV waves, through the buffer nobody reads in the last
     // iteration, and the rows' log-sum-exp.
-    Exchange<kFP8, NRB>& xe = sm.x[T & 1];
+    WsExchange<KV, NRB>& xe = sm.x[T & 1];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       if (lane < 16) xe.row[16 * (2 * w + j) + lane] = lsum[j][0];
@@ -398,10 +546,14 @@ __global__ __launch_bounds__(512, 1) void prefill_ws_kernel(PrefillArgs a) {
     barrier();
     for (int i = 0; i < T; ++i) {
       barrier_publish();  // V of tile i has landed (the copying waves waited for it); P(i) is visible
-      pv_ws<NRB>(o, (const lds_t*)&sm.v[0][0] + (i % kPipeStages) * kTile, sm.x[i & 1], d);
+      const lds_t* vt = (const lds_t*)&sm.v[0][0] + (i % kPipeStages) * kTile;
+      if constexpr (KV == kFP8)
+        pv_ws<NRB>(o, vt, sm.x[i & 1], d);
+      else
+        pv_ws_bf16<NRB>(o, vt, sm.x[i & 1], d);
     }
     barrier_publish();
-    const Exchange<kFP8, NRB>& xe = sm.x[T & 1];
+    const WsExchange<KV, NRB>& xe = sm.x[T & 1];
     const float vds = load_scale(a.kv.v_ds);
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb) {
@@ -424,17 +576,17 @@ __global__ __launch_bounds__(512, 1) void prefill_ws_kernel(PrefillArgs a) {
 
 int prefill_tile_tokens(int q_dtype, int kv_dtype, int r) {
   if (r <= 0) return 0;
-  return (q_dtype == kFP8 && kv_dtype == kFP8) ? kPipeRows / r : 64 / r;
+  return q_dtype == kv_dtype ? kPipeRows / r : 64 / r;
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, int q_dtype, int kv_dtype, int q_tiles, hipStream_t s) {
   dim3 grid(q_tiles, a.kv.num_kv_heads, a.num_seqs);
   if (q_dtype == kFP8 && kv_dtype == kFP8)
-    hipLaunchKernelGGL(prefill_ws_kernel, grid, dim3(512), 0, s, a);
-  else if (q_dtype == kBF16 && kv_dtype == kFP8)
-    hipLaunchKernelGGL((prefill_kernel<kBF16, kFP8, 4>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL(prefill_ws_kernel<kFP8>, grid, dim3(512), 0, s, a);
+  else if (q_dtype == kBF16 && kv_dtype == kBF16)
+    hipLaunchKernelGGL(prefill_ws_kernel<kBF16>, grid, dim3(512), 0, s, a);
   else
-    hipLaunchKernelGGL((prefill_kernel<kBF16, kBF16, 4>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((prefill_kernel<kBF16, kFP8, 4>), grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

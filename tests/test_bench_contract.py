@@ -36,7 +36,7 @@ def test_counter_records_name_the_benchmarked_kernel():
     with open(bench.COUNTERS) as fh:
         db = json.load(fh)
     for config, rec in db.items():
-        k = bench.KERNELS[bench.kernel_key(config)]
+        k = bench.KERNELS[bench.mode_of(config)]
         assert rec["kernel"] == k["main"], f"{config}: counters of {rec['kernel']}, bench times {k['main']}"
         assert rec["hbm_bytes_per_launch"] > 0
 

@@ -124,13 +124,31 @@ PREFILL_CASES = [
     ("fp8_6to1", dict(seed=[37], lq=[90, 23], lk=[250, 23], hq=6, hkv=1, q=w.FP8, kv=w.FP8)),
     ("fp8_3to1_2kv", dict(seed=[38], lq=[85], lk=[300], hq=6, hkv=2, q=w.FP8, kv=w.FP8)),
     ("bf16q_3to1", dict(seed=[39], lq=[40], lk=[140], hq=3, hkv=1, q=w.BF16, kv=w.FP8)),
+    # bf16 queries and keys (the warp-specialised kernel on 32-key tiles):
+    # ragged lengths, other ratios, head-major and larger pages.
+    ("bf16_bf16_varlen", dict(seed=[131], lq=[37, 64, 5], lk=[87, 264, 5], hq=8, hkv=1, q=w.BF16, kv=w.BF16)),
+    ("bf16_bf16_hnd_page64", dict(seed=[132], lq=[65], lk=[390], hq=8, hkv=1, q=w.BF16, kv=w.BF16, layout="HND",
+                                  page=64)),
+    ("bf16_bf16_pure_causal", dict(seed=[133], lq=[129], lk=[129], hq=8, hkv=1, q=w.BF16, kv=w.BF16)),
+    ("bf16_bf16_6to1", dict(seed=[134], lq=[90, 23], lk=[250, 23], hq=6, hkv=1, q=w.BF16, kv=w.BF16)),
+    ("bf16_bf16_3to1_2kv", dict(seed=[135], lq=[85], lk=[300], hq=6, hkv=2, q=w.BF16, kv=w.BF16)),
+    ("bf16_bf16_16to1", dict(seed=[136], lq=[33], lk=[500], hq=16, hkv=1, q=w.BF16, kv=w.BF16)),
+    ("bf16_bf16_page32", dict(seed=[137], lq=[50], lk=[333], hq=8, hkv=1, q=w.BF16, kv=w.BF16, page=32)),
+    # A negative scale (the kernels keep their score multiplier positive by
+    # negating the queries) and a zero scale (every visible key weighs the same).
+    ("bf16_bf16_negative_scale", dict(seed=[138], lq=[60], lk=[200], hq=8, hkv=1, q=w.BF16, kv=w.BF16,
+                                      scale=-1.0 / 16.0)),
+    ("fp8_negative_scale", dict(seed=[139], lq=[60], lk=[200], hq=8, hkv=1, q=w.FP8, kv=w.FP8, scale=-1.0 / 16.0)),
+    ("bf16_bf16_zero_scale", dict(seed=[140], lq=[60], lk=[200], hq=8, hkv=1, q=w.BF16, kv=w.BF16, scale=0.0)),
+    ("fp8_zero_scale", dict(seed=[141], lq=[60], lk=[200], hq=8, hkv=1, q=w.FP8, kv=w.FP8, scale=0.0)),
 ]
 
 
 @pytest.mark.parametrize("name,c", PREFILL_CASES, ids=[n for n, _ in PREFILL_CASES])
 def test_prefill_parity(name, c):
     p = w.make_causal(name, c["seed"], c["lq"], c["lk"], c["hq"], c["hkv"], kv_dtype=c["kv"], q_dtype=c["q"],
-                      page_size=c.get("page", 16), layout=c.get("layout", "NHD"), mode="prefill")
+                      page_size=c.get("page", 16), layout=c.get("layout", "NHD"), mode="prefill",
+                      softmax_scale=c.get("scale", 1.0 / 16.0))
     _check(w.poison_unused(p))
 
 
@@ -280,6 +298,7 @@ LSE_NULL_CASES = [
     ("verify_bf16_unsplit", "verify", 0),
     ("prefill_fp8", "prefill", None),
     ("prefill_bf16q", "prefill", None),
+    ("prefill_bf16_bf16", "prefill", None),
     ("sparse_fp8_split", "sparse", None),
     ("sparse_bf16_unsplit", "sparse", None),
 ]
@@ -296,7 +315,8 @@ def test_lse_null(name, mode, split):
                           kv_sigma=0.5 if kv == w.FP8 else 1.0, mode="verify")
     elif mode == "prefill":
         qd = w.FP8 if name == "prefill_fp8" else w.BF16
-        p = w.make_causal(name, [72], [70, 9], [300, 9], 8, 1, kv_dtype=w.FP8, q_dtype=qd, mode="prefill")
+        kvd = w.BF16 if name == "prefill_bf16_bf16" else w.FP8
+        p = w.make_causal(name, [72], [70, 9], [300, 9], 8, 1, kv_dtype=kvd, q_dtype=qd, mode="prefill")
     else:
         kv = w.FP8 if "fp8" in name else w.BF16
         p = w.make_sparse(name, [73], [6], [3000], 24, 2, 900, kv_dtype=kv)
