@@ -255,10 +255,11 @@ struct TilePV<kFP8, 1> {
   }
 };
 
-// Scores of several 16-row blocks of one wave on the same tile (FP8 queries
-// and keys): each K fragment read from LDS feeds one MFMA per row block, so
-// the LDS reads of a tile are shared by NRB * 16 query rows.
-template <int NRB, int NMB>
+// Scores of several 16-row blocks of one wave on the same tile (FP8 keys):
+// each K fragment read from LDS feeds one MFMA per row block (two with a
+// split bf16 query, QSPLIT: the high and the low part), so the LDS reads of a
+// tile are shared by NRB * 16 query rows.
+template <int NRB, int NMB, bool QSPLIT = false>
 __device__ __forceinline__ void tile_scores_rows(const lds_t* kt, const QFragT<kFP8> (&qf)[NRB],
                                                  f32x4 (&s)[NRB][NMB]) {
   using G = TileGeom<kFP8>;
@@ -270,14 +271,35 @@ __device__ __forceinline__ void tile_scores_rows(const lds_t* kt, const QFragT<k
     for (int mb = 0; mb < NMB; ++mb) s[rb][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
+    if constexpr (!QSPLIT) {
 #pragma unroll
-    for (int mb = 0; mb < NMB; ++mb) {
-      const int key = mb * 16 + n;
-      const i32x4 a0 = lds_load<i32x4>(kt + G::off(key, 8 * h + 2 * gq));
-      const i32x4 a1 = lds_load<i32x4>(kt + G::off(key, 8 * h + 2 * gq + 1));
-      const i32x8 a = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+      for (int mb = 0; mb < NMB; ++mb) {
+        const int key = mb * 16 + n;
+        const i32x4 a0 = lds_load<i32x4>(kt + G::off(key, 8 * h + 2 * gq));
+        const i32x4 a1 = lds_load<i32x4>(kt + G::off(key, 8 * h + 2 * gq + 1));
+        const i32x8 a = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
 #pragma unroll
-      for (int rb = 0; rb < NRB; ++rb) s[rb][mb] = mfma_fp8_scaled(a, qf[rb].hi[h], s[rb][mb], kScaleOne);
+        for (int rb = 0; rb < NRB; ++rb) s[rb][mb] = mfma_fp8_scaled(a, qf[rb].hi[h], s[rb][mb], kScaleOne);
+      }
+    } else {
+      // Every high-part product of the half before the low parts, so no
+      // product waits on the one just issued into the same accumulator.
+      i32x8 a[NMB];
+#pragma unroll
+      for (int mb = 0; mb < NMB; ++mb) {
+        const int key = mb * 16 + n;
+        const i32x4 a0 = lds_load<i32x4>(kt + G::off(key, 8 * h + 2 * gq));
+        const i32x4 a1 = lds_load<i32x4>(kt + G::off(key, 8 * h + 2 * gq + 1));
+        a[mb] = i32x8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+      }
+#pragma unroll
+      for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb) s[rb][mb] = mfma_fp8_scaled(a[mb], qf[rb].hi[h], s[rb][mb], kScaleOne);
+#pragma unroll
+      for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb) s[rb][mb] = mfma_fp8_scaled(a[mb], qf[rb].lo[h], s[rb][mb], kScaleLo);
     }
   }
 }

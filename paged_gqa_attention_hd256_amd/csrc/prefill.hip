@@ -8,79 +8,22 @@
 // kernel, with no gather to contiguous memory first (ROCm/ATOM PR #2830, recipe
 // commit).  Workgroups are ordered longest first.
 //
-// FP8 queries with FP8 keys (the pages' FP8 FMHA) and bf16 queries with bf16
-// keys run the warp-specialised prefill_ws_kernel below; bf16 queries against
-// FP8 keys run prefill_kernel, the tile step shared with verify.
+// One warp-specialised kernel serves FP8 queries with FP8 keys (the pages'
+// FP8 FMHA), bf16 queries with bf16 keys, and bf16 queries against FP8 keys.
 #include <type_traits>
 
 #include "causal_stream.h"
 
 namespace pga {
 
-// bf16 queries: NW = 4 waves per workgroup (64 rows).
-template <int QDT, int KV, int NW>
-__global__ __launch_bounds__(64 * NW, KV == kFP8 ? 2 : 1) void prefill_kernel(PrefillArgs a) {
-  __shared__ CausalSmem<KV, NW> sm;
-  const int g = blockIdx.y, b = blockIdx.z;
-  const int tok0 = a.cu_q[b];
-  const int lq = min(a.cu_q[b + 1] - tok0, a.max_q_len);
-  const int lk = min(a.cu_k[b + 1] - a.cu_k[b], a.max_kv_len);
-  // Longest first: block 0 takes the last query tile, which sees the most keys.
-  const int t_lo = (gridDim.x - 1 - blockIdx.x) * a.tile_tokens;
-  if (t_lo >= lq) return;
-  const int t_hi = min(t_lo + a.tile_tokens, lq);
-  const int k_hi = lk - lq + t_hi;  // one past the last visible key of the tile
-  const int rows = a.r * (t_hi - t_lo);
-
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int lane = lane_id();
-  const int n = lane & 15;
-  const int rho = 16 * w + n;  // this lane's softmax row
-  const bool row_ok = rho < rows;
-  const int tq = row_ok ? rho / a.r : 0;
-  const int head = g * a.r + (row_ok ? rho - tq * a.r : 0);
-  const int64_t tok = tok0 + t_lo + tq;
-  const int32_t* bt_row = a.kv.bt + (int64_t)b * a.kv.bt_stride;
-  const int2 first = first_pages<NW>(a.kv, bt_row, 0, k_hi);
-  QFragT<KV> qf;
-  load_q<QDT, KV>(qf, a.q, tok, a.hq, head, row_ok);
-  const float c2 = a.c2_base * load_scale(a.q_ds) * load_scale(a.kv.k_ds);
-  const int klim = row_ok ? min(lk - lq + t_lo + tq, k_hi - 1) : -1;
-  const int min_lim = min(lk - lq + t_lo, k_hi - 1);
-  const bool live = 16 * w < rows;
-  RowStat rs;
-  rs.init();
-  f32x4 o[16];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  f32x4 lsum = {0.f, 0.f, 0.f, 0.f};
-  stream_keys<false>(sm, a.kv, bt_row, g, 0, k_hi, first,
-              SplitTile<QDT, KV, NW>{qf, c2 * qf.rscale, klim, min_lim, live, rs, o, lsum, sm.x});
-  const float lrow = finish_rows(lsum, live, sm.x);
-  if (row_ok && (lane >> 4) == 0 && a.lse)
-    a.lse[tok * a.hq + head] = lrow > 0.f ? (rs.m + log2f(lrow)) * kLn2 : kNegInf;
-  const float vds = load_scale(a.kv.v_ds);
-#pragma unroll
-  for (int rb = 0; rb < NW; ++rb) {
-    const int rr = 16 * rb + n;
-    if (rr < rows) {
-      const int t2 = rr / a.r;
-      const float l = sm.x.row[rr];
-      store_share_bf16<NW>(o, rb, l > 0.f ? vds / l : 0.f,
-                           a.out + ((tok0 + t_lo + t2) * (int64_t)a.hq + g * a.r + rr - t2 * a.r) * kHeadDim);
-    }
-  }
-}
-
 // ---------------------------------------------------------------------------
-// Queries and keys of one encoding (FP8 and FP8, or bf16 and bf16): a
-// warp-specialised, software-pipelined tile loop.  Tiles hold 64 FP8 or 32
+// A warp-specialised, software-pipelined tile loop.  Tiles hold 64 FP8 or 32
 // bf16 keys (16 KB of K and of V either way).
 //
-// The tile step above runs a tile's QK^T, softmax and PV back to back in every
-// wave, so a wave's vector work (scaling, maxima, exponentials, conversions)
-// and its matrix work follow each other.  Here the eight waves of a workgroup
-// (128 rows, one workgroup per CU) split by kind of work:
+// The verify kernel's tile step runs a tile's QK^T, softmax and PV back to
+// back in every wave, so a wave's vector work (scaling, maxima, exponentials,
+// conversions) and its matrix work follow each other.  Here the eight waves
+// of a workgroup (128 rows, one workgroup per CU) split by kind of work:
 //  - waves 0 .. 3 compute scores and softmax, wave w for rows 32 w .. 32 w + 31
 //    (two 16-row blocks sharing every K fragment read from LDS), and issue
 //    every tile copy (a quarter of the rows of each K and V tile per wave);
@@ -388,8 +331,11 @@ __device__ __forceinline__ void pv_ws_bf16(f32x4 (&o)[4 * NRB], const lds_t* vt,
   }
 }
 
-template <int KV>
+template <int QDT, int KV>
 __global__ __launch_bounds__(512, 1) void prefill_ws_kernel(PrefillArgs a) {
+  // bf16 queries against FP8 keys: each row split exactly into two FP8 parts
+  // (its own power-of-two scale), two products per K fragment.
+  constexpr bool QSPLIT = QDT == kBF16 && KV == kFP8;
   constexpr int NRB = kPipeRows / 16;  // row blocks of the workgroup
   constexpr int TK = kWsKeys<KV>;      // keys per tile
   __shared__ PipeSmem<KV, NRB> sm;
@@ -465,14 +411,17 @@ __global__ __launch_bounds__(512, 1) void prefill_ws_kernel(PrefillArgs a) {
       const int rr = 16 * (2 * w + j) + n;
       const bool ok = rr < rows;
       const int t2 = ok ? rr / a.r : 0;
-      load_q<KV, KV>(qf[j], a.q, tok0 + t_lo + t2, a.hq, g * a.r + (ok ? rr - t2 * a.r : 0), ok);
+      load_q<QDT, KV>(qf[j], a.q, tok0 + t_lo + t2, a.hq, g * a.r + (ok ? rr - t2 * a.r : 0), ok);
       klim[j] = ok ? min(lk - lq + t_lo + t2, k_hi - 1) : -1;
       if (flip) {
         if constexpr (KV == kFP8) {
 #pragma unroll
           for (int h = 0; h < 2; ++h)
 #pragma unroll
-            for (int i = 0; i < 8; ++i) qf[j].hi[h][i] ^= (int)0x80808080u;
+            for (int i = 0; i < 8; ++i) {
+              qf[j].hi[h][i] ^= (int)0x80808080u;
+              if constexpr (QSPLIT) qf[j].lo[h][i] ^= (int)0x80808080u;
+            }
         } else {
 #pragma unroll
           for (int ks = 0; ks < 8; ++ks)
@@ -481,6 +430,11 @@ __global__ __launch_bounds__(512, 1) void prefill_ws_kernel(PrefillArgs a) {
       }
     }
     c2 = fmaxf(fabsf(c2), 1e-30f);  // a zero scale: every score counts the same
+    float c2row[2] = {c2, c2};       // per row block: times the split's row scale (this lane's row)
+    if constexpr (QSPLIT) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) c2row[j] *= qf[j].rscale;
+    }
     const int min_lim = min(lk - lq + t_lo, k_hi - 1);  // tiles ending at or below it need no mask
     RowStat rs[2];
     f32x4 lsum[2];
@@ -494,15 +448,15 @@ __global__ __launch_bounds__(512, 1) void prefill_ws_kernel(PrefillArgs a) {
       const lds_t* kt = (const lds_t*)&sm.k[0][0] + (j % kPipeStages) * kTile;
       WsExchange<KV, NRB>& x = sm.x[j & 1];
       if constexpr (KV == kFP8) {
-        tile_scores_rows<2, 4>(kt, qf, s);
+        tile_scores_rows<2, 4, QSPLIT>(kt, qf, s);
 #pragma unroll
         for (int r = 0; r < 2; ++r)
-          softmax_ws<decltype(masked)::value>(rs[r], lsum[r], s[r], c2, klim[r] - TK * j, x, 2 * w + r);
+          softmax_ws<decltype(masked)::value>(rs[r], lsum[r], s[r], c2row[r], klim[r] - TK * j, x, 2 * w + r);
       } else {
         tile_scores_rows_bf16<2, 2>(kt, qf, s);
 #pragma unroll
         for (int r = 0; r < 2; ++r)
-          softmax_ws_bf16<decltype(masked)::value>(rs[r], lsum[r], s[r], c2, klim[r] - TK * j, x, 2 * w + r);
+          softmax_ws_bf16<decltype(masked)::value>(rs[r], lsum[r], s[r], c2row[r], klim[r] - TK * j, x, 2 * w + r);
       }
     };
     wait_vmcnt<0>();
@@ -574,19 +528,19 @@ __global__ __launch_bounds__(512, 1) void prefill_ws_kernel(PrefillArgs a) {
   }
 }
 
-int prefill_tile_tokens(int q_dtype, int kv_dtype, int r) {
-  if (r <= 0) return 0;
-  return q_dtype == kv_dtype ? kPipeRows / r : 64 / r;
-}
+// Every pair of encodings runs the 128-row kernel.
+int prefill_tile_tokens(int, int, int r) { return r > 0 ? kPipeRows / r : 0; }
 
 hipError_t launch_prefill(const PrefillArgs& a, int q_dtype, int kv_dtype, int q_tiles, hipStream_t s) {
   dim3 grid(q_tiles, a.kv.num_kv_heads, a.num_seqs);
   if (q_dtype == kFP8 && kv_dtype == kFP8)
-    hipLaunchKernelGGL(prefill_ws_kernel<kFP8>, grid, dim3(512), 0, s, a);
+    hipLaunchKernelGGL((prefill_ws_kernel<kFP8, kFP8>), grid, dim3(512), 0, s, a);
   else if (q_dtype == kBF16 && kv_dtype == kBF16)
-    hipLaunchKernelGGL(prefill_ws_kernel<kBF16>, grid, dim3(512), 0, s, a);
+    hipLaunchKernelGGL((prefill_ws_kernel<kBF16, kBF16>), grid, dim3(512), 0, s, a);
+  else if (q_dtype == kBF16 && kv_dtype == kFP8)
+    hipLaunchKernelGGL((prefill_ws_kernel<kBF16, kFP8>), grid, dim3(512), 0, s, a);
   else
-    hipLaunchKernelGGL((prefill_kernel<kBF16, kFP8, 4>), grid, dim3(256), 0, s, a);
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

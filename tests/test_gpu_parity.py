@@ -141,6 +141,12 @@ PREFILL_CASES = [
     ("fp8_negative_scale", dict(seed=[139], lq=[60], lk=[200], hq=8, hkv=1, q=w.FP8, kv=w.FP8, scale=-1.0 / 16.0)),
     ("bf16_bf16_zero_scale", dict(seed=[140], lq=[60], lk=[200], hq=8, hkv=1, q=w.BF16, kv=w.BF16, scale=0.0)),
     ("fp8_zero_scale", dict(seed=[141], lq=[60], lk=[200], hq=8, hkv=1, q=w.FP8, kv=w.FP8, scale=0.0)),
+    # bf16 queries against FP8 keys (each query row split into two FP8 parts).
+    ("bf16q_fp8kv_negative_scale", dict(seed=[142], lq=[60], lk=[200], hq=8, hkv=1, q=w.BF16, kv=w.FP8,
+                                        scale=-1.0 / 16.0)),
+    ("bf16q_fp8kv_varlen_hnd64", dict(seed=[143], lq=[37, 64, 5], lk=[87, 264, 5], hq=8, hkv=1, q=w.BF16,
+                                      kv=w.FP8, layout="HND", page=64)),
+    ("bf16q_fp8kv_16to1", dict(seed=[144], lq=[33], lk=[500], hq=16, hkv=1, q=w.BF16, kv=w.FP8)),
 ]
 
 

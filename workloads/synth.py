@@ -347,6 +347,7 @@ _CONFIGS = {
     "sparse_fp8_3to1": 10,
     "prefix_prefill_32k_bf16": 11,
     "prefix_prefill_32k_page64_hnd": 12,
+    "prefix_prefill_32k_bf16q": 13,
 }
 
 
@@ -404,6 +405,9 @@ def config(name: str) -> Problem:
     if name == "prefix_prefill_32k_bf16":
         # The 16k-new / 32k-context prefill in bf16 (Q, K and V).
         return make_causal(name, [c, 0], [16384], [32768], 8, 1, kv_dtype=BF16, q_dtype=BF16, mode="prefill")
+    if name == "prefix_prefill_32k_bf16q":
+        # The 16k-new / 32k-context prefill with bf16 queries against the FP8 pool.
+        return make_causal(name, [c, 0], [16384], [32768], 8, 1, kv_dtype=FP8, q_dtype=BF16, mode="prefill")
     if name == "prefix_prefill_32k_page64_hnd":
         # The FP8 16k / 32k prefill over 64-token pages laid out [pages, heads, slots, d].
         return make_causal(name, [c, 0], [16384], [32768], 8, 1, kv_dtype=FP8, q_dtype=FP8, page_size=64,
