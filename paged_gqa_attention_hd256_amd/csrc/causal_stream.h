@@ -1,6 +1,6 @@
-// Streaming of a contiguous key range of one (sequence, kv head) through LDS,
-// shared by the verify and prefill kernels, and the attention of the
-// workgroup's 16 * NW query rows on each streamed tile (NW = 4 or 8 waves).
+// Streaming of a contiguous key range of one (sequence, kv head) through LDS
+// for the verify kernels, and the attention of the workgroup's 16 * NW query
+// rows on each streamed tile (NW = 4 waves).
 //
 // A workgroup of NW waves walks keys [k_lo, k_hi) in 64-key tiles.  Each wave
 // fetches 64 / NW rows of every tile (K and V) by 16-byte global->LDS DMA into
@@ -71,11 +71,9 @@ __device__ __forceinline__ int2 first_pages(const KvArgs& kv, const int32_t* bt_
   return int2{k_hi > k_lo ? scalar_load(bt_row + p0) : 0, k_hi > k_lo + 64 ? scalar_load(bt_row + p1) : 0};
 }
 
-// STREAM: the keys are read exactly once (speculative verify, where each
-// piece of each history belongs to one workgroup), so their copies use the
-// non-temporal cache policy; the prefill re-reads every key from L2 for each
-// query tile and keeps the default policy.
-template <bool STREAM, int KV, int NW, class Tile>
+// The keys are read exactly once (each piece of each history belongs to one
+// workgroup), so their copies use the non-temporal cache policy.
+template <int KV, int NW, class Tile>
 __device__ __forceinline__ void stream_keys(CausalSmem<KV, NW>& sm, const KvArgs& kv, const int32_t* bt_row, int g,
                                             int k_lo, int k_hi, int2 first, const Tile& tile) {
   using G = TileGeom<KV>;
@@ -121,12 +119,12 @@ __device__ __forceinline__ void stream_keys(CausalSmem<KV, NW>& sm, const KvArgs
                                    : (uint64_t)(uintptr_t)g_zero16;
     if (!page_ok) {
 #pragma unroll
-      for (int u = 0; u < kDma; ++u) dma16_off<STREAM>(pbase, 0u, dst + (kRowsPerWave * w + u * kRowsPerDma) * G::kRowBytes);
+      for (int u = 0; u < kDma; ++u) dma16_off<true>(pbase, 0u, dst + (kRowsPerWave * w + u * kRowsPerDma) * G::kRowBytes);
     } else if (tb + 64 <= k_hi) {  // every key of the tile exists
       const uint64_t tbase = pbase + (uint64_t)((tb & pmask) * (unsigned)st);
 #pragma unroll
       for (int u = 0; u < kDma; ++u)
-        dma16_off<STREAM>(tbase, lane_off[u], dst + (kRowsPerWave * w + u * kRowsPerDma) * G::kRowBytes);
+        dma16_off<true>(tbase, lane_off[u], dst + (kRowsPerWave * w + u * kRowsPerDma) * G::kRowBytes);
     } else {
 #pragma unroll
       for (int u = 0; u < kDma; ++u) {
@@ -134,7 +132,7 @@ __device__ __forceinline__ void stream_keys(CausalSmem<KV, NW>& sm, const KvArgs
         const int row = row0 + lane / G::kChunks;
         const unsigned chunk = (lane % G::kChunks) ^ (row & (G::kChunks - 1));
         const unsigned key = (unsigned)min(tb + row, k_hi - 1);
-        dma16_off<STREAM>(pbase, (key & pmask) * (unsigned)st + chunk * 16, dst + row0 * G::kRowBytes);
+        dma16_off<true>(pbase, (key & pmask) * (unsigned)st + chunk * 16, dst + row0 * G::kRowBytes);
       }
     }
   };

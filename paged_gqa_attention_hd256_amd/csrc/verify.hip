@@ -148,7 +148,7 @@ __device__ __forceinline__ void verify_piece(const VerifyArgs& a, CausalSmem<KV,
 #pragma unroll
   for (int i = 0; i < 16; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   f32x4 lsum = {0.f, 0.f, 0.f, 0.f};
-  stream_keys<true>(sm, a.kv, bt_row, g, k_lo, k_hi, first,
+  stream_keys(sm, a.kv, bt_row, g, k_lo, k_hi, first,
               SplitTile<kBF16, KV, 4>{qf, c2 * qf.rscale, klim, min_lim, live, rs, o, lsum, sm.x});
   const float lrow = finish_rows(lsum, live, sm.x);
   if (row_ok && gq == 0) {
@@ -214,7 +214,7 @@ template <int KV>
 __device__ __forceinline__ void gather_piece(const VerifyArgs& a, CausalSmem<KV, 4>& sm, int b, int g, int k_lo,
                                              int k_hi, int2 first) {
   u32x4 acc = {0u, 0u, 0u, 0u};
-  stream_keys<true>(sm, a.kv, a.kv.bt + (int64_t)b * a.kv.bt_stride, g, k_lo, k_hi, first, SumTile<KV>{&acc, k_hi});
+  stream_keys(sm, a.kv, a.kv.bt + (int64_t)b * a.kv.bt_stride, g, k_lo, k_hi, first, SumTile<KV>{&acc, k_hi});
   uint32_t t = acc[0] + acc[1] + acc[2] + acc[3];
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) t += (uint32_t)__shfl_xor((int)t, off);
