@@ -20,21 +20,33 @@
 //
 // LDS tile layout: row = key, row bytes RB = 256 * elt, stored in 16-byte
 // chunks whose position is XOR-swizzled by the key: logical chunk c of key k
-// sits at chunk c ^ (k & (RB / 16 - 1)).
+// sits at chunk c ^ (k & (RB / 16 - 1)).  SPREAD (bf16 rows, 32 chunks): at
+// c ^ (2 k mod 32) instead, which keeps the two chunks of one 16-column block
+// (2d, 2d + 1) apart for neighbouring keys, so the 16-bit transpose reads of
+// V (keys 4 (lane / 16) + e, both chunks of a block) and the row reads of K
+// (16 keys, one chunk each) hit distinct banks.
 #pragma once
 
 #include "pga_device.h"
 
 namespace pga {
 
-template <int KV>
+template <int KV, bool SPREAD = false>
 struct TileGeom {
   static constexpr int kElt = (KV == kFP8) ? 1 : 2;
   static constexpr int kRowBytes = kHeadDim * kElt;  // 256 or 512
   static constexpr int kChunks = kRowBytes / 16;     // 16 or 32
   template <int TK>
   static constexpr int tile_bytes() { return TK * kRowBytes; }  // one of K or V
-  __device__ static __forceinline__ int swz(int key, int chunk) { return chunk ^ (key & (kChunks - 1)); }
+  // The key's part of the swizzle: logical chunk c of key k sits at c ^ xor_of(k).
+  // The tile copies compute the same term in place.
+  __device__ static __forceinline__ int xor_of(int key) {
+    if constexpr (SPREAD)
+      return (2 * key) & (kChunks - 1);
+    else
+      return key & (kChunks - 1);
+  }
+  __device__ static __forceinline__ int swz(int key, int chunk) { return chunk ^ xor_of(key); }
   __device__ static __forceinline__ int off(int key, int chunk) { return key * kRowBytes + (swz(key, chunk) << 4); }
 };
 

@@ -67,7 +67,7 @@ struct PipeSmem {
 // Copies of this wave's rows of one tile of K or V (global -> LDS).
 template <int KV, int NW>
 struct TileCopy {
-  using G = TileGeom<KV>;
+  using G = TileGeom<KV, KV == kBF16>;  // bf16 tiles use the spread swizzle
   static constexpr int kKeys = kWsKeys<KV>;
   static constexpr int kRowsPerWave = kKeys / NW;
   static constexpr int kRowsPerDma = 1024 / G::kRowBytes;
@@ -85,7 +85,7 @@ struct TileCopy {
 #pragma unroll
     for (int u = 0; u < kDma; ++u) {
       const int row = kRowsPerWave * w + u * kRowsPerDma + lane / G::kChunks;
-      const unsigned chunk = (lane % G::kChunks) ^ (row & (G::kChunks - 1));
+      const unsigned chunk = (lane % G::kChunks) ^ ((KV == kFP8 ? row : 2 * row) & (G::kChunks - 1));
       lane_k[u] = (row & pmask) * (unsigned)kv.k_st + chunk * 16;
       lane_v[u] = (row & pmask) * (unsigned)kv.v_st + chunk * 16;
     }
@@ -121,7 +121,7 @@ struct TileCopy {
       for (int u = 0; u < kDma; ++u) {
         const int row0 = kRowsPerWave * w + u * kRowsPerDma;
         const int row = row0 + lane / G::kChunks;
-        const unsigned chunk = (lane % G::kChunks) ^ (row & (G::kChunks - 1));
+        const unsigned chunk = (lane % G::kChunks) ^ ((KV == kFP8 ? row : 2 * row) & (G::kChunks - 1));
         const unsigned key = (unsigned)min(tb + row, k_hi - 1);
         dma16_off(pbase, (key & pmask) * (unsigned)st + chunk * 16, dst + row0 * G::kRowBytes);
       }
@@ -223,7 +223,7 @@ __device__ __forceinline__ void pv_ws(f32x4 (&o)[4 * NRB], const lds_t* vt, cons
 template <int NRB, int NMB>
 __device__ __forceinline__ void tile_scores_rows_bf16(const lds_t* kt, const QFragT<kBF16> (&qf)[NRB],
                                                       f32x4 (&s)[NRB][NMB]) {
-  using G = TileGeom<kBF16>;
+  using G = TileGeom<kBF16, true>;
   const int lane = lane_id();
   const int n = lane & 15, gq = lane >> 4;
 #pragma unroll
@@ -289,7 +289,7 @@ __device__ __forceinline__ void softmax_ws_bf16(RowStat& rs, f32x4& lsum, f32x4 
 template <int NRB>
 __device__ __forceinline__ void pv_ws_bf16(f32x4 (&o)[4 * NRB], const lds_t* vt, const WsExchange<kBF16, NRB>& x,
                                            int d) {
-  using G = TileGeom<kBF16>;
+  using G = TileGeom<kBF16, true>;
   const int lane = lane_id();
   const int gq = lane >> 4, sl = lane & 15;
   int any = 0;
