@@ -354,19 +354,21 @@ __global__ __launch_bounds__(256, (KV == kFP8) ? 2 : 1) void verify_gather_kerne
 }
 
 // Log-sum-exp merge of the partial rows of every (sequence, kv head) unit that
-// verify_kernel did not write directly.  One wave per query row: the lanes
-// take one piece each (the lse of up to 64 pieces in one load, their maximum
-// and weight sum by wave reductions), then the whole wave reads the pieces'
-// rows with the loads of several pieces in flight at once; batches of 64
-// pieces are combined online.  Pieces with lse = -inf (no visible key) get
-// weight 0.
+// verify_kernel did not write directly.  One wave per pair of query rows, one
+// row per half-wave (16 bytes of stored partial per lane and piece): the
+// lanes take one piece each (the lse values of up to 64 pieces for both rows
+// in one load each, their maxima and weight sums by wave reductions), then
+// every half-wave reads its row of the pieces with the loads of several
+// pieces in flight at once; batches of 64 pieces are combined online.  Pieces
+// with lse = -inf (no visible key) get weight 0.
 template <int KV>
 __global__ __launch_bounds__(256) void verify_merge_kernel(VerifyArgs a) {
   const int hkv = a.kv.num_kv_heads;
   const int u = blockIdx.x;
   const int b = u / hkv, g = u - (u / hkv) * hkv;
-  const int rho = blockIdx.y * 4 + (threadIdx.x >> 6);
+  const int rho_a = blockIdx.y * 8 + 2 * (threadIdx.x >> 6);  // this wave's rows: rho_a, rho_a + 1
   const int lane = lane_id();
+  const int half = lane >> 5, hl = lane & 31;
   // Where the unit lies in the flattened order, as verify_kernel recorded it:
   // loaded together with the sequence's lengths so the two latencies overlap
   // (the addresses are in bounds for every unit; the values are used only
@@ -378,15 +380,43 @@ __global__ __launch_bounds__(256) void verify_merge_kernel(VerifyArgs a) {
   if (sw.tiles == 0) return;
   const int tok0 = scalar_load(a.cu_q + b);
   const int lq = min(scalar_load(a.cu_q + b + 1) - tok0, a.max_q_len);
-  if (rho >= min(a.r * lq, a.rows_cap)) return;
+  const int rows = min(a.r * lq, a.rows_cap);
+  if (rho_a >= rows) return;
+  const bool b_ok = rho_a + 1 < rows;
+  const int rho_b = b_ok ? rho_a + 1 : rho_a;    // a missing second row reads the first (in bounds)
+  const int rho = half ? rho_b : rho_a;          // this lane's row
   const int S = kSegStartCost + a.seg_tiles;
   if (sw.segs == 1 && (tu + kSegStartCost) / tpw == (tu + kSegStartCost + sw.tiles - 1) / tpw)
     return;  // written directly
+  constexpr int kBatch = (KV == kFP8) ? 16 : 8;  // pieces whose rows are in flight at once
+  // This lane's 8 head dimensions of its row in piece slot sl, as stored (fp16
+  // for FP8 V, fp32 for BF16 V), and widened to fp32.
+  using Raw = std::conditional_t<KV == kFP8, i32x4, f32x8>;
+  auto load_part = [&](int sl) -> Raw {
+    const int64_t off = ((int64_t)sl * a.rows_cap + rho) * kHeadDim + 8 * hl;
+    if constexpr (KV == kFP8)
+      return *reinterpret_cast<const i32x4*>(static_cast<const uint16_t*>(a.ws_o) + off);
+    else
+      return *reinterpret_cast<const f32x8*>(static_cast<const float*>(a.ws_o) + off);
+  };
+  auto widen = [](Raw r) -> f32x8 {
+    if constexpr (KV == kFP8) {
+      const f16x8 h = __builtin_bit_cast(f16x8, r);
+      f32x8 x;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) x[i] = (float)h[i];
+      return x;
+    } else {
+      return r;
+    }
+  };
   // Pieces per segment: lane s takes segment s (up to 64 segments at once),
   // so piece j's segment is found by comparisons against a prefix sum instead
   // of a division per segment per piece.
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  float mx = kNegInf, wsum = 0.f;
+  f32x8 acc;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+  float mx_a = kNegInf, ws_a = 0.f, mx_b = kNegInf, ws_b = 0.f;
   for (int s0 = 0; s0 < sw.segs; s0 += 64) {
     const int sl = s0 + lane;
     int first = 0, cnt = 0;
@@ -399,24 +429,6 @@ __global__ __launch_bounds__(256) void verify_merge_kernel(VerifyArgs a) {
     const int excl = incl - cnt;
     const int nseg = min(64, sw.segs - s0);
     const int np = __builtin_amdgcn_readfirstlane(__shfl(incl, nseg - 1));  // pieces of these segments
-    // This lane's 4 head dimensions of the row in piece slot sl, as stored
-    // (fp16 for FP8 V, fp32 for BF16 V), and widened to fp32.
-    using Raw = std::conditional_t<KV == kFP8, uint2, f32x4>;
-    auto load_part = [&](int sl) -> Raw {
-      const int64_t off = ((int64_t)sl * a.rows_cap + rho) * kHeadDim + 4 * lane;
-      if constexpr (KV == kFP8)
-        return *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(a.ws_o) + off);
-      else
-        return *reinterpret_cast<const f32x4*>(static_cast<const float*>(a.ws_o) + off);
-    };
-    auto widen = [](Raw r) -> f32x4 {
-      if constexpr (KV == kFP8) {
-        const f16x4 h = __builtin_bit_cast(f16x4, r);
-        return f32x4{(float)h[0], (float)h[1], (float)h[2], (float)h[3]};
-      } else {
-        return r;
-      }
-    };
     for (int c = 0; c < np; c += 64) {
       // Piece j's segment and that segment's first piece and slot, taken with
       // scalar reads of lane k's values: a lane shuffle here would sit under
@@ -429,49 +441,69 @@ __global__ __launch_bounds__(256) void verify_merge_kernel(VerifyArgs a) {
         if (j >= ek) { sj = k; fj = fk; ej = ek; }
       }
       const int slot = j < np ? su + s0 + sj + fj + (j - ej) : -1;
-      const float ls = slot >= 0 ? a.ws_lse[(int64_t)slot * a.rows_cap + rho] : kNegInf;
-      // The rows of up to 16 pieces are requested with their lse values (one
+      const float ls_a = slot >= 0 ? a.ws_lse[(int64_t)slot * a.rows_cap + rho_a] : kNegInf;
+      const float ls_b = slot >= 0 ? a.ws_lse[(int64_t)slot * a.rows_cap + rho_b] : kNegInf;
+      // The rows of the first pieces are requested with their lse values (one
       // round trip for the usual piece counts); no load past the last piece.
       const int n = min(64, np - c);
-      Raw v[16];
+      Raw v[kBatch];
 #pragma unroll
-      for (int k = 0; k < 16; ++k) {
+      for (int k = 0; k < kBatch; ++k) {
         v[k] = Raw{};
-        if (k < n) v[k] = load_part(__builtin_amdgcn_readlane(slot, k));  // wave-uniform
+        if (k < n) v[k] = load_part(__builtin_amdgcn_readlane(slot, k));  // wave-uniform slot
       }
-      // Online merge of this batch of pieces into (mx, wsum, acc).
-      const float mb = wave_max(ls);
-      if (mb == kNegInf) continue;
-      const float m_new = fmaxf(mx, mb);
-      const float scale = mx == kNegInf ? 0.f : __expf(mx - m_new);
-      acc *= scale;
-      wsum *= scale;
-      mx = m_new;
-      const float wgt = ls == kNegInf ? 0.f : __expf(ls - mx);
-      wsum += wave_sum(wgt);
-      for (int q = 0; q < n; q += 16) {
+      // Online merge of this batch of pieces into each row's (mx, ws) and acc.
+      const float mb_a = wave_max(ls_a), mb_b = wave_max(ls_b);
+      if (mb_a == kNegInf && mb_b == kNegInf) continue;
+      float sc_a = 1.f, sc_b = 1.f;
+      if (mb_a != kNegInf) {
+        const float m_new = fmaxf(mx_a, mb_a);
+        sc_a = mx_a == kNegInf ? 0.f : __expf(mx_a - m_new);
+        ws_a *= sc_a;
+        mx_a = m_new;
+      }
+      if (mb_b != kNegInf) {
+        const float m_new = fmaxf(mx_b, mb_b);
+        sc_b = mx_b == kNegInf ? 0.f : __expf(mx_b - m_new);
+        ws_b *= sc_b;
+        mx_b = m_new;
+      }
+      acc *= half ? sc_b : sc_a;
+      const float wg_a = (ls_a == kNegInf || mx_a == kNegInf) ? 0.f : __expf(ls_a - mx_a);
+      const float wg_b = (ls_b == kNegInf || mx_b == kNegInf) ? 0.f : __expf(ls_b - mx_b);
+      ws_a += wave_sum(wg_a);
+      ws_b += wave_sum(wg_b);
+      for (int q = 0; q < n; q += kBatch) {
         if (q > 0) {
 #pragma unroll
-          for (int k = 0; k < 16; ++k) {
+          for (int k = 0; k < kBatch; ++k) {
             v[k] = Raw{};
-            if (q + k < n) v[k] = load_part(__builtin_amdgcn_readlane(slot, q + k));  // wave-uniform
+            if (q + k < n) v[k] = load_part(__builtin_amdgcn_readlane(slot, q + k));  // wave-uniform slot
           }
         }
 #pragma unroll
-        for (int k = 0; k < 16; ++k) {
-          const float wq = q + k < n ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wgt), q + k)) : 0.f;
-          if (wq != 0.f) acc += wq * widen(v[k]);
+        for (int k = 0; k < kBatch; ++k) {
+          float wq = 0.f;
+          if (q + k < n) {
+            const float wa = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wg_a), q + k));
+            const float wb = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wg_b), q + k));
+            wq = half ? wb : wa;
+          }
+          if (wq != 0.f) acc += wq * widen(v[k]);  // a zero weight never touches the slot's data
         }
       }
     }
   }
-  const float inv = wsum > 0.f ? load_scale(a.kv.v_ds) / wsum : 0.f;
+  if (half && !b_ok) return;
+  const float ws = half ? ws_b : ws_a, mx = half ? mx_b : mx_a;
+  const float inv = ws > 0.f ? load_scale(a.kv.v_ds) / ws : 0.f;
   const int t = rho / a.r;
   const int head = g * a.r + (rho - t * a.r);
   const int64_t tok = tok0 + t;
-  uint16_t* op = a.out + (tok * a.hq + head) * kHeadDim + 4 * lane;
-  *reinterpret_cast<uint2*>(op) = make_uint2(pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv));
-  if (lane == 0 && a.lse) a.lse[tok * a.hq + head] = wsum > 0.f ? mx + logf(wsum) : kNegInf;
+  uint16_t* op = a.out + (tok * a.hq + head) * kHeadDim + 8 * hl;  // out is 8-byte aligned: two 8-byte stores
+  reinterpret_cast<uint2*>(op)[0] = make_uint2(pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv));
+  reinterpret_cast<uint2*>(op)[1] = make_uint2(pack_bf16x2(acc[4] * inv, acc[5] * inv), pack_bf16x2(acc[6] * inv, acc[7] * inv));
+  if (hl == 0 && a.lse) a.lse[tok * a.hq + head] = ws > 0.f ? mx + logf(ws) : kNegInf;
 }
 
 // The merge of the plan-free mode: unit u's pieces are slots u * P + k for
@@ -562,16 +594,19 @@ hipError_t launch_verify_gather(const VerifyArgs& a, int kv_dtype, int num_wg, h
 }
 
 hipError_t launch_verify_merge(const VerifyArgs& a, int kv_dtype, int num_wg, hipStream_t s) {
-  dim3 grid(a.num_seqs * a.kv.num_kv_heads, (a.rows_cap + 3) / 4);
+  const unsigned units = (unsigned)(a.num_seqs * a.kv.num_kv_heads);
   if (a.static_tiles > 0) {
+    const dim3 grid(units, (a.rows_cap + 3) / 4);  // one row per wave
     if (kv_dtype == kFP8)
       hipLaunchKernelGGL(verify_merge_tiles_kernel<kFP8>, grid, dim3(256), 0, s, a);
     else
       hipLaunchKernelGGL(verify_merge_tiles_kernel<kBF16>, grid, dim3(256), 0, s, a);
-  } else if (kv_dtype == kFP8) {
-    hipLaunchKernelGGL(verify_merge_kernel<kFP8>, grid, dim3(256), 0, s, a);
   } else {
-    hipLaunchKernelGGL(verify_merge_kernel<kBF16>, grid, dim3(256), 0, s, a);
+    const dim3 grid(units, (a.rows_cap + 7) / 8);  // two rows per wave
+    if (kv_dtype == kFP8)
+      hipLaunchKernelGGL(verify_merge_kernel<kFP8>, grid, dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL(verify_merge_kernel<kBF16>, grid, dim3(256), 0, s, a);
   }
   return hipGetLastError();
 }
