@@ -174,9 +174,16 @@ uint64_t next_quant_tag() {
 // (query token x kv head x 16-row block) would not fill the GPU, each row's
 // index list is cut into pieces (multiples of 32 entries, at least 256 per
 // piece, at most kMaxSparseSplits), processed by separate waves and merged by
-// log-sum-exp.
-constexpr int64_t kSparseTargetJobs = 4096;  // ~4 waves per SIMD of a 256-CU device
+// log-sum-exp.  The piece count minimises a round count times a piece
+// length: the sparse kernels hold one workgroup per CU, so on a 256-CU part
+// the waves run in rounds of 2,048 (FP8, eight waves per workgroup) or 1,024
+// (BF16, four); a call's time is its rounds times one piece's tiles plus the
+// cost of starting a piece (kSparsePieceStartTiles).  A few jobs past a round
+// boundary cost a whole extra round, which the job count alone does not see.
+constexpr int64_t kSparseTargetJobs = 4096;  // jobs at or past this fill the GPU: no split
 constexpr int32_t kMaxSparseSplits = 32;
+constexpr int64_t kSparseRoundWavesFp8 = 2048, kSparseRoundWavesBf16 = 1024;
+constexpr int64_t kSparsePieceStartTiles = 3;  // query load, table translation, pipeline fill
 struct SparsePlan {
   int32_t splits = 1, split_len = 1;
   size_t ws_o_bytes = 0, ws_bytes = 0;
@@ -184,11 +191,21 @@ struct SparsePlan {
 bool plan_sparse(int32_t hq, int32_t hkv, int32_t num_q_tokens, int32_t num_selected, SparsePlan& p) {
   if (hq <= 0 || hkv <= 0 || hq % hkv != 0 || num_q_tokens < 0 || num_selected < 0) return false;
   const int64_t jobs = int64_t(num_q_tokens) * hkv * cdiv(hq / hkv, 16);
-  int64_t splits = 1;
-  if (jobs > 0 && jobs < kSparseTargetJobs && num_selected > 0)
-    splits = std::max<int64_t>(1, std::min<int64_t>({cdiv(kSparseTargetJobs, jobs), kMaxSparseSplits,
-                                                     cdiv(num_selected, 256)}));
-  const int64_t len = std::max<int64_t>(32, (cdiv(num_selected, splits) + 31) / 32 * 32);
+  auto piece_len = [&](int64_t s) { return std::max<int64_t>(32, (cdiv(num_selected, s) + 31) / 32 * 32); };
+  int64_t len = piece_len(1);
+  if (jobs > 0 && jobs < kSparseTargetJobs && num_selected > 0) {
+    const int64_t s_max = std::max<int64_t>(1, std::min<int64_t>(kMaxSparseSplits, cdiv(num_selected, 256)));
+    int64_t best = -1;
+    for (int64_t s = 1; s <= s_max; ++s) {
+      const int64_t l = piece_len(s), pieces = cdiv(num_selected, l);
+      const int64_t rounds = cdiv(jobs * pieces, kSparseRoundWavesFp8) + cdiv(jobs * pieces, kSparseRoundWavesBf16);
+      const int64_t cost = rounds * (cdiv(l, 16) + kSparsePieceStartTiles);
+      if (best < 0 || cost < best) {
+        best = cost;
+        len = l;
+      }
+    }
+  }
   p.splits = num_selected > 0 ? static_cast<int32_t>(cdiv(num_selected, len)) : 1;
   p.split_len = static_cast<int32_t>(len);
   p.ws_o_bytes = p.ws_bytes = 0;

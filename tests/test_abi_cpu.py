@@ -218,13 +218,27 @@ def test_sparse_rejects_invalid_arguments(lib):
 
 
 def test_sparse_split_plan(lib):
+    def cdiv(a, b):
+        return -(-a // b)
+
     def expect(hq, hkv, ntok, nsel):
-        jobs = ntok * hkv * -(-(hq // hkv) // 16)
-        splits = 1
+        # The piece count with the fewest rounds x piece tiles on a 256-CU part
+        # (2,048 FP8 and 1,024 BF16 waves per round; 3 tiles to start a piece).
+        jobs = ntok * hkv * cdiv(hq // hkv, 16)
+
+        def piece_len(s):
+            return max(32, cdiv(cdiv(nsel, s), 32) * 32)
+
+        length = piece_len(1)
         if 0 < jobs < 4096 and nsel > 0:
-            splits = max(1, min(-(-4096 // jobs), 32, -(-nsel // 256)))
-        length = max(32, -(-(-(-nsel // splits)) // 32) * 32)
-        splits = -(-nsel // length) if nsel > 0 else 1
+            costs = []
+            for s in range(1, max(1, min(32, cdiv(nsel, 256))) + 1):
+                ln = piece_len(s)
+                pieces = cdiv(nsel, ln)
+                rounds = cdiv(jobs * pieces, 2048) + cdiv(jobs * pieces, 1024)
+                costs.append((rounds * (cdiv(ln, 16) + 3), s, ln))
+            length = min(costs)[2]
+        splits = cdiv(nsel, length) if nsel > 0 else 1
         ws = 0
         if splits > 1:
             slots = ntok * hq * splits
@@ -238,6 +252,9 @@ def test_sparse_split_plan(lib):
         assert lib.sparse_paged_attn_workspace_bytes(*args) == ws, args
     assert lib.sparse_paged_attn_splits(24, 2, 8, 2048) == 8
     assert lib.sparse_paged_attn_splits(24, 2, 8192, 2051) == 1      # the large-row workload: no split
+    # 260 rows: 7 pieces (455 FP8 workgroups, two rounds of 256 CUs) rather
+    # than 8 (520 workgroups: a third round for 8 of them).
+    assert lib.sparse_paged_attn_splits(24, 2, 260, 2051) == 7
     assert lib.sparse_paged_attn_splits(25, 2, 8, 64) == 0          # invalid head counts
 
 
